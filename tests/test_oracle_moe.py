@@ -1,0 +1,253 @@
+"""Pins of the oracle's layer steps: grouping, gather, grouped GEMM, SwiGLU, scatter, layer.
+
+Each pin comes from outside the oracle: a brute-force scan, exact rational arithmetic,
+reductions to a gather, known constants of the logistic function, or the invariants
+the pages test ([GG] "Proof": row invariance, fused w13 == separate, determinism).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import moe, nvfp4
+
+# --------------------------------------------------------------------------- grouping
+
+
+def _brute_group(a_expert, a_src, a_dst, E, S, T):
+    """Counting-sort by scanning experts in order and assignments in order."""
+    rows = []
+    for e in range(E):
+        for j in range(len(a_expert)):
+            if a_expert[j] == e and 0 <= a_src[j] < S and 0 <= a_dst[j] < T:
+                rows.append(j)
+    return rows
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_group_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    E, S, T, R = 7, 9, 5, 40
+    a_expert = rng.integers(-1, E + 1, R)
+    a_src = rng.integers(-1, S + 1, R)
+    a_dst = rng.integers(0, T + 1, R)
+    a_w = rng.random(R).astype(np.float32)
+    g = moe.group_rows(a_expert, a_src, a_dst, a_w, E, S, T)
+    rows = _brute_group(a_expert, a_src, a_dst, E, S, T)
+    Rv = len(rows)
+    assert g["offsets"][E] == Rv and g["offsets"][0] == 0
+    assert list(g["row_src"][:Rv]) == [a_src[j] for j in rows]
+    assert list(g["row_dst"][:Rv]) == [a_dst[j] for j in rows]
+    assert list(g["row_w"][:Rv]) == [a_w[j] for j in rows]
+    for e in range(E):
+        seg = g["row_expert"][g["offsets"][e]:g["offsets"][e + 1]]
+        assert np.all(seg == e)
+        assert g["offsets"][e + 1] - g["offsets"][e] == sum(
+            1 for j in rows if a_expert[j] == e)
+    assert np.all(g["row_src"][Rv:] == -1) and np.all(g["row_w"][Rv:] == 0)
+    # error bits
+    want_err = 0
+    if np.any((a_expert < 0) | (a_expert >= E)):
+        want_err |= moe.ERR_EXPERT
+    if np.any((a_src < 0) | (a_src >= S)):
+        want_err |= moe.ERR_SRC
+    if np.any((a_dst < 0) | (a_dst >= T)):
+        want_err |= moe.ERR_DST
+    assert g["err"] == want_err
+    # token CSR: each token's rows ascending, covering exactly the valid rows
+    seen = []
+    for t in range(T):
+        lst = list(g["tok_rows"][g["tok_off"][t]:g["tok_off"][t + 1]])
+        assert lst == sorted(lst)
+        assert all(g["row_dst"][i] == t for i in lst)
+        seen += lst
+    assert sorted(seen) == list(range(Rv))
+
+
+def test_gather_exact_and_dropped_rows_zero():
+    x = np.arange(12, dtype=np.uint16).reshape(3, 4) + 0x3F00
+    out = moe.gather_rows(x, np.array([2, 0, -1, 2]))
+    assert np.array_equal(out[0], x[2]) and np.array_equal(out[1], x[0])
+    assert not out[2].any() and np.array_equal(out[3], x[2])
+
+
+# --------------------------------------------------------------------------- GEMM
+E2M1_HAND = [0, 1, 2, 3, 4, 6, 8, 12]      # 2 * e2m1 magnitude, codes 0..7
+
+
+def _val(nib_row, sc_row, k):
+    """Exact value of element k of an NVFP4 row, decoded by hand (no oracle code)."""
+    byte = int(nib_row[k // 2])
+    code = (byte >> 4) if k % 2 else (byte & 0xF)
+    mag = Fraction(E2M1_HAND[code & 7], 2)
+    s = int(sc_row[k // 16])
+    e, m = (s >> 3) & 15, s & 7
+    scale = Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    if s & 0x80:
+        scale = -scale
+    return (-mag if code & 8 else mag) * scale
+
+
+def _rand_nvfp4(rng, rows, K, scale_lo=0x00, scale_hi=0x7E):
+    nib = rng.integers(0, 256, (rows, K // 2)).astype(np.uint8)
+    sc = rng.integers(scale_lo, scale_hi + 1, (rows, K // 16)).astype(np.uint8)
+    return nib, sc
+
+
+def test_grouped_gemm_exact_against_rational_brute_force():
+    """K <= 256: every product and partial sum is exact in float64 (exponent span of the
+    products is 43 bits, +8 bits of sum), so the oracle must equal exact rationals."""
+    rng = np.random.default_rng(11)
+    E, N, K = 3, 5, 64
+    offsets = np.array([0, 2, 2, 5])             # expert 1 is empty
+    aq, as_ = _rand_nvfp4(rng, 5, K)
+    W = [_rand_nvfp4(rng, N, K) for _ in range(E)]
+    acc = moe.grouped_gemm(aq, as_, offsets, lambda e: W[e], N, K)
+    for e in range(E):
+        for i in range(offsets[e], offsets[e + 1]):
+            for n in range(N):
+                s = sum(_val(aq[i], as_[i], k) * _val(W[e][0][n], W[e][1][n], k)
+                        for k in range(K))
+                assert Fraction(acc[i, n]) == s, (e, i, n)
+
+
+def test_grouped_gemm_one_hot_weights_is_a_gather():
+    """Weight row n holds a single 1.0 (code 2, scale 0x38) at column perm[n]: the GEMM
+    returns the activation's value at that column."""
+    rng = np.random.default_rng(12)
+    N = K = 32
+    perm = rng.permutation(K)
+    codes = np.zeros((N, K), dtype=np.uint8)
+    codes[np.arange(N), perm] = 2
+    nib = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    sc = np.full((N, K // 16), 0x38, np.uint8)
+    aq, as_ = _rand_nvfp4(rng, 3, K, 0x20, 0x50)
+    acc = moe.grouped_gemm(aq, as_, np.array([0, 3]), lambda e: (nib, sc), N, K)
+    for i in range(3):
+        for n in range(N):
+            assert Fraction(acc[i, n]) == _val(aq[i], as_[i], perm[n])
+
+
+def test_fused_w13_equals_separate_and_row_invariance():
+    """[GG] "Proof": the fused gate|up operand gives the gate-only and up-only results,
+    and a row's output does not depend on which rows share its group."""
+    rng = np.random.default_rng(13)
+    I, K = 16, 256
+    gate = _rand_nvfp4(rng, I, K)
+    up = _rand_nvfp4(rng, I, K)
+    fused = (np.concatenate([gate[0], up[0]]), np.concatenate([gate[1], up[1]]))
+    aq, as_ = _rand_nvfp4(rng, 4, K)
+    off = np.array([0, 4])
+    f = moe.grouped_gemm(aq, as_, off, lambda e: fused, 2 * I, K)
+    g = moe.grouped_gemm(aq, as_, off, lambda e: gate, I, K)
+    u = moe.grouped_gemm(aq, as_, off, lambda e: up, I, K)
+    assert np.array_equal(f[:, :I], g) and np.array_equal(f[:, I:], u)
+    for i in range(4):
+        alone = moe.grouped_gemm(aq[i:i + 1], as_[i:i + 1], np.array([0, 1]),
+                                 lambda e: fused, 2 * I, K)
+        assert np.array_equal(alone[0], f[i])
+
+
+# --------------------------------------------------------------------------- SwiGLU
+SIGMOID_1 = 0.7310585786300049     # 1 / (1 + e^-1)
+SIGMOID_2 = 0.8807970779778823
+SIGMOID_3 = 0.9525741268224334
+
+
+def _swiglu_one(gate, up, g_gate=1.0, g_up=1.0, gs=1.0):
+    acc = np.array([[gate, up]], dtype=np.float64)
+    h = moe.swiglu(acc, np.array([0, 1]), np.array([g_gate]), np.array([g_up]),
+                   np.array([gs], np.float32), 1)
+    return nvfp4.bf16_bits_to_f32(h)[0, 0]
+
+
+def _bf16(v):
+    return nvfp4.bf16_bits_to_f32(nvfp4.f64_to_bf16_bits(v))
+
+
+def test_swiglu_known_values_and_halves():
+    assert _swiglu_one(0.0, 5.0) == 0.0                        # silu(0) = 0
+    assert _swiglu_one(1.0, 1.0) == _bf16(SIGMOID_1)
+    assert _swiglu_one(2.0, 3.0) == _bf16(3 * 2 * SIGMOID_2)   # silu on the gate half
+    assert _swiglu_one(3.0, 2.0) == _bf16(2 * 3 * SIGMOID_3)   # ... not on the up half
+    assert _swiglu_one(40.0, 0.5) == 20.0                      # silu(z) -> z
+    v = _swiglu_one(-40.0, 1.0)
+    assert v < 0 and abs(v) < 1e-15                            # silu(z) -> 0-
+
+
+def test_swiglu_globals_apply_per_half():
+    """[MF] "Different globals on the two halves", option (a): the gate global scales the
+    gate half, the up global the up half, and the row global both."""
+    assert _swiglu_one(1.0, 1.0, g_gate=2.0, g_up=1.0) == _bf16(2 * SIGMOID_2)
+    assert _swiglu_one(1.0, 1.0, g_gate=1.0, g_up=2.0) == _bf16(2 * SIGMOID_1)
+    assert _swiglu_one(0.5, 0.5, gs=2.0) == _bf16(SIGMOID_1)
+
+
+# --------------------------------------------------------------------------- scatter
+def test_scatter_single_row_exact_and_empty_token():
+    y = np.array([[1.0, -3.0, 0.25], [5.0, 6.0, 7.0]])
+    offsets = np.array([0, 1, 2])
+    row_w = np.array([0.5, 0.25], np.float32)
+    g_down = np.array([2.0, 4.0], np.float32)
+    gs = np.array([4.0, 0.5], np.float32)
+    tok_off = np.array([0, 1, 1, 2])                 # token 1 has no rows
+    tok_rows = np.array([0, 1])
+    out = nvfp4.bf16_bits_to_f32(moe.scatter_add(y, offsets, row_w, g_down, gs, tok_off,
+                                                 tok_rows, 3))
+    assert list(out[0]) == [4.0, -12.0, 1.0]          # 0.5*2*4 * y[0]
+    assert not out[1].any()
+    assert list(out[2]) == [2.5, 3.0, 3.5]            # 0.25*4*0.5 * y[1]
+
+
+def test_scatter_is_linear_on_exact_values():
+    rng = np.random.default_rng(3)
+    y1 = rng.integers(-8, 8, (4, 6)).astype(np.float64)
+    y2 = rng.integers(-8, 8, (4, 6)).astype(np.float64)
+    args = (np.array([0, 2, 4]), np.array([1, 0.5, 2, 1], np.float32),
+            np.array([1, 2], np.float32), np.ones(4, np.float32),
+            np.array([0, 3, 4]), np.array([0, 1, 3, 2]), 2)
+    f = lambda y: nvfp4.bf16_bits_to_f32(moe.scatter_add(y, *args)).astype(np.float64)
+    assert np.array_equal(f(y1 + y2), f(y1) + f(y2))
+
+
+# --------------------------------------------------------------------------- layer
+def _tiny_layer_inputs(seed, T=6, E=4, H=64, I=32, k=2):
+    rng = np.random.default_rng(seed)
+    W13 = [_rand_nvfp4(rng, 2 * I, H, 0x18, 0x38) for _ in range(E)]
+    W2 = [_rand_nvfp4(rng, H, I, 0x18, 0x38) for _ in range(E)]
+    x = nvfp4.f64_to_bf16_bits(rng.standard_normal((T, H)))
+    a_expert = np.concatenate([rng.choice(E, k, replace=False) for _ in range(T)])
+    a_src = np.repeat(np.arange(T), k)
+    a_w = rng.random(T * k).astype(np.float32)
+    gl = lambda v: np.full(E, v, np.float32)
+    return dict(x=x, a_expert=a_expert, a_src=a_src, a_dst=a_src.copy(), a_w=a_w,
+                W13=W13, W2=W2, g=(gl(4.65e-5), gl(3.78e-5), gl(4.2e-5)), E=E, H=H, I=I, k=k)
+
+
+def _run(d, sel=None):
+    T = d["x"].shape[0]
+    idx = np.arange(len(d["a_expert"])) if sel is None else sel
+    return moe.layer_forward(d["x"], d["a_expert"][idx], d["a_src"][idx], d["a_dst"][idx],
+                             d["a_w"][idx], T, lambda e: d["W13"][e], lambda e: d["W2"][e],
+                             *d["g"], d["E"], d["H"], d["I"])
+
+
+def test_layer_batch_parity_and_determinism():
+    """[GG] "Proof" (batch parity, five repeated calls): a token's output computed in a
+    batch equals its output computed with only its own rows; repeated calls agree."""
+    d = _tiny_layer_inputs(21)
+    full = _run(d)
+    for _ in range(2):
+        assert np.array_equal(_run(d), full)
+    k = d["k"]
+    for t in (0, 3, 5):
+        alone = _run(d, np.arange(t * k, t * k + k))
+        assert np.array_equal(alone[t], full[t])
+        assert not np.delete(alone, t, axis=0).any()
+
+
+def test_layer_output_scale_is_sane():
+    """Output ~ sum_k w * g_down * (quantized h) . w2; nonzero and finite."""
+    d = _tiny_layer_inputs(22)
+    out = nvfp4.bf16_bits_to_f32(_run(d))
+    assert np.all(np.isfinite(out)) and np.abs(out).max() > 0

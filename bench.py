@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 routed-expert MoE layer on one MI355X.
+
+A step is one moe_layer_forward call over one synthetic batch: grouping, gather +
+quantize, w13 grouped GEMM, SwiGLU + re-quantize, w2 grouped GEMM, scatter-add — every
+step of the path, inputs and packed weights already resident in HBM.
+
+Metric (the pages' own byte model, table "Bytes decide it before the kernel runs" of the
+2026-09-06 page): weight-stream GB/s = active experts x 14,155,776 B / layer time.
+
+Prints ONE JSON line.  Also times the dominant kernel (the w13 grouped GEMM) with HIP
+events on its own stream over a loop of launches on the layer's real inputs, and the CPU
+oracle on a bounded sample of the same workload (cpu_baseline).
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer ms + weight-stream HBM GB/s (% of peak), 288 experts, 570/2303 rows"
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+W13_BYTES_PER_EXPERT = 2 * 2048 * 4096 * 9 // 16   # 9,437,184
+LAYER_BYTES_PER_EXPERT = 3 * 2048 * 4096 * 9 // 16  # 14,155,776
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="ragged570",
+                   choices=["ragged570", "ragged2303", "zipf512", "decode1"])
+    p.add_argument("--also", default="ragged2303",
+                   help="second workload timed in the same run ('' for none)")
+    p.add_argument("--flags", type=int, default=None, help="GEMM path (0 auto, 1 GEMV, 2 MFMA)")
+    p.add_argument("--gemv-max-rows", type=int, default=None)
+    p.add_argument("--kernel-iters", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-experts", type=int, default=24,
+                   help="experts in the oracle's bounded sample")
+    return p.parse_args()
+
+
+def time_layer(dl, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        dl.forward()
+    torch.cuda.synchronize()
+    per = []
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        start.record()
+        dl.forward()
+        stop.record()
+        stop.synchronize()
+        per.append(start.elapsed_time(stop))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return float(np.median(per)), float(np.min(per)), float(np.max(per)), wall
+
+
+def time_w13(dl, iters):
+    """Average duration of one w13 grouped-GEMM launch (grouped_gemm_nvfp4) on the layer's
+    own quantized activations, HIP events on the launch stream."""
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    wl = dl.wl
+    R, E, H, I, T, S = wl.R, wl.E, wl.H, wl.I, wl.T, wl.S
+    dev = torch.device("cuda")
+    e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+    xg, off = e((R, H), torch.int16), e((E + 1,), torch.int32)
+    rs, rd, rw = e((R,), torch.int32), e((R,), torch.int32), e((R,), torch.float32)
+    to, tr, err = e((T + 1,), torch.int32), e((R,), torch.int32), e((1,), torch.int32)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        B.moe_gather_rows(dl.x, S, H, dl.a_expert, dl.a_src, dl.a_dst, dl.a_w, R, E, T, xg, off,
+                          rs, rd, rw, to, tr, err)
+        xq, xs, xgs = e((R, H // 2), torch.uint8), e((R, H // 16), torch.uint8), e((R,), torch.float32)
+        B.nvfp4_quantize_rows(xg, R, H, xq, xs, xgs)
+        acc = e((R, 2 * I), torch.float32)
+        flags, gmax = dl.desc.flags, dl.desc.gemv_max_rows
+        for _ in range(3):
+            B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gmax)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(iters):
+            B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gmax)
+        stop.record(stream)
+    stop.synchronize()
+    return start.elapsed_time(stop) / iters
+
+
+def cpu_baseline(wl, n_experts):
+    """The CPU oracle on a bounded sample: the rows of the first n_experts active experts
+    (their whole layer: quantize, both GEMMs, SwiGLU, scatter), reported in the metric's
+    unit (weight-stream GB/s over the sample) plus the layer time it extrapolates to."""
+    from oracle import moe as omoe
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    active = wl.active_experts()
+    keep = set(active[:n_experts])
+    sel = np.array([j for j in range(wl.R) if int(wl.a_expert[j]) in keep], dtype=np.int64)
+    t0 = time.perf_counter()
+    omoe.layer_forward(wl.x, wl.a_expert[sel], wl.a_src[sel], wl.a_dst[sel], wl.a_w[sel], wl.T,
+                       wl.w13, wl.w2, wl.g_gate, wl.g_up, wl.g_down, wl.E, wl.H, wl.I)
+    dt = time.perf_counter() - t0
+    nbytes = len(keep) * LAYER_BYTES_PER_EXPERT
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": "%s: rows of the first %d of %d active experts (%d of %d expert-rows), whole "
+                  "layer in the numpy float64 oracle; %.2f s, extrapolates to %.0f ms per layer; "
+                  "host %d logical CPUs (%s); numpy dequantization is single-threaded, BLAS "
+                  "matrix-vector products use %d threads"
+                  % (wl.name, len(keep), len(active), len(sel), wl.R, dt,
+                     dt * 1e3 * len(active) / len(keep), os.cpu_count() or 0, cpu_model,
+                     blas_threads),
+    }
+
+
+def run_workload(name, args, weights=None):
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    wl = W.make_workload(name)
+    kw = {}
+    if args.flags is not None:
+        kw["flags"] = args.flags
+    if args.gemv_max_rows is not None:
+        kw["gemv_max_rows"] = args.gemv_max_rows
+    if weights is None:
+        log("packing %d experts (w13 + w2, %.3f GB)" % (wl.E, wl.E * LAYER_BYTES_PER_EXPERT / 1e9))
+        t0 = time.perf_counter()
+        weights = (L.pack_expert_weights(wl.w13, wl.E, 2 * wl.I, wl.H),
+                   L.pack_expert_weights(wl.w2, wl.E, wl.H, wl.I))
+        log("packed in %.1f s" % (time.perf_counter() - t0))
+    dl = L.DeviceLayer(wl, weights=weights, **kw)
+    med, lo, hi, wall = time_layer(dl, args.steps, args.warmup)
+    err = dl.device_error()
+    if err:
+        raise RuntimeError("device error word %d" % err)
+    n_act = len(wl.active_experts())
+    wbytes = n_act * LAYER_BYTES_PER_EXPERT
+    w13_ms = time_w13(dl, args.kernel_iters)
+    res = {
+        "workload": name, "expert_rows": wl.R, "tokens": wl.T, "active_experts": n_act,
+        "layer_ms_median": med, "layer_ms_min": lo, "layer_ms_max": hi, "layer_ms_wall": wall,
+        "weight_bytes": wbytes, "weight_GBps": wbytes / (med * 1e-3) / 1e9,
+        "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "w13_gemm_ms": w13_ms,
+        "w13_GBps": n_act * W13_BYTES_PER_EXPERT / (w13_ms * 1e-3) / 1e9,
+        "gemm_path": {"flags": dl.desc.flags, "gemv_max_rows": dl.desc.gemv_max_rows},
+    }
+    log(json.dumps(res))
+    return wl, dl, res, weights
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
+              "(see the sharding notes in DESIGN.md); got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from nvfp4_block_scaled_gather_amd import binding as B
+    B.load()
+    wl, dl, res, weights = run_workload(args.workload, args)
+    also = {}
+    if args.also and args.also != args.workload and wl.E == 288:
+        _, dl2, res2, _ = run_workload(args.also, args, weights)
+        also[args.also] = res2
+        del dl2
+
+    # dominant kernel: the w13 grouped GEMM (one grouped_gemm_nvfp4 call)
+    R, H, I = wl.R, wl.H, wl.I
+    alg_bytes = (res["active_experts"] * W13_BYTES_PER_EXPERT     # weights, read once
+                 + R * H * 9 // 16                                  # NVFP4 activations
+                 + R * 2 * I * 4)                                   # fp32 outputs
+    achieved = alg_bytes / (res["w13_gemm_ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "kernel": "grouped_gemm_nvfp4 (w13, N=4096, K=4096) on %s" % args.workload,
+                "bytes_per_launch": alg_bytes}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl, args.cpu_experts)
+    ms = res["layer_ms_median"]
+    line = {
+        "metric": METRIC, "value": res["weight_GBps"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4",
+        "data": "synthetic",
+        "config": {"workload": "%s: 288 experts, H=4096, I=2048, %d expert-rows, %d tokens"
+                               % (args.workload, R, wl.T),
+                   "experts": wl.E, "hidden": H, "intermediate": I, "expert_rows": R,
+                   "active_experts": res["active_experts"], "weight_bytes": res["weight_bytes"],
+                   "parallelism": "single GPU"},
+        "layer_ms": ms, "layer_ms_min": res["layer_ms_min"], "layer_ms_max": res["layer_ms_max"],
+        "frac_of_hbm_peak": res["frac_of_hbm_peak"],
+        "w13_gemm_ms": res["w13_gemm_ms"], "w13_weight_GBps": res["w13_GBps"],
+        "roofline": roofline, "cpu_baseline": cpu, "also": also,
+        "host": platform.node(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

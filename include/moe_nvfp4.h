@@ -1,0 +1,238 @@
+/* moe_nvfp4.h — C ABI of the NVFP4 routed-expert MoE layer library for AMD MI355X (gfx950).
+ *
+ * The library implements the routed-expert loop that the page "The CUTLASS grouped GEMM
+ * beats the scalar GEMV loop at every M, M=1 included, so the crossover is 1"
+ * (gabewillen.github.io/rocket, posts/runtime, 2026-09-07) lays out in its section
+ * "What changed":
+ *
+ *   gather -> NVFP4 quantize -> grouped GEMM over the fused gate|up weights (w13)
+ *   -> SwiGLU with separate gate / up globals -> NVFP4 quantize -> grouped GEMM over w2
+ *   -> scatter-add weighted by router weight * down global.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless the comment says "host".  bf16 values are passed
+ *   as their uint16_t bit patterns.  The caller allocates and owns every buffer; the
+ *   library allocates nothing, keeps no global state and is reentrant.
+ * - Every call is asynchronous on the given stream: it validates its arguments on the
+ *   host, enqueues kernels and returns.  Only moe_get_device_error() synchronizes.
+ * - Return value: MOE_OK (0) or a negative moe_status.  Argument errors (null pointers
+ *   with a non-zero size, unsupported shapes, misalignment, a workspace that is too
+ *   small) are detected on the host BEFORE anything is enqueued.  A failed launch returns
+ *   MOE_EHIP.  moe_last_error() gives the text of the last failure on the calling thread.
+ * - Data errors that only the device can see (an expert id, source row or output row out
+ *   of range) never fault: the offending assignment is dropped and a bit is set in a
+ *   device error word (MOE_ERR_*), which moe_get_device_error() reads back.
+ * - Inputs must be finite; NaN / Inf inputs give unspecified (but deterministic) output.
+ * - Results are deterministic: repeated calls with identical inputs give bit-identical
+ *   outputs (no floating-point atomics anywhere).
+ *
+ * NVFP4 (page "Fusing the MoE layer's two grouped GEMMs is worth 4%, and a CUDA graph
+ * already collects it", gabewillen.github.io/rocket, posts/kernels, 2026-09-06, table
+ * "Bytes decide it before the kernel runs" and section "Different globals on the two
+ * halves"): e2m1 elements, two per byte with the even element in the low nibble; one
+ * e4m3fn scale byte per 16 consecutive elements along K; one fp32 global per activation
+ * row and per weight projection.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument: null pointer, negative size, misalignment */
+  MOE_EUNSUPPORTED = -2,  /* shape this library cannot run (see each call's limits) */
+  MOE_EHIP = -3,          /* a HIP launch or runtime call failed */
+  MOE_EWORKSPACE = -4     /* workspace smaller than the matching *_workspace_bytes() */
+} moe_status;
+
+/* flags of grouped_gemm_nvfp4 / moe_layer_desc: how each expert group is computed */
+enum {
+  MOE_PATH_AUTO = 0,        /* groups of <= gemv_max_rows rows: GEMV; larger: MFMA */
+  MOE_PATH_FORCE_GEMV = 1,  /* every group on the wavefront-reduction GEMV */
+  MOE_PATH_FORCE_MFMA = 2   /* every group on the MFMA path */
+};
+
+/* bits of the device error word */
+enum { MOE_ERR_EXPERT = 1, MOE_ERR_SRC = 2, MOE_ERR_DST = 4 };
+
+/* ----------------------------------------------------------------------------------
+ * Weight packing (load time).  The grouped GEMM reads expert weights in a layout of
+ * this library's own, written once when the weights are loaded — the counterpart of
+ * the expert-cache fill in section "The seam CUTLASS forced open" of the 2026-09-07
+ * page, which writes the scale layout its GEMM needs once per projection.
+ *
+ * nvfp4_packed_weight_bytes: host query, bytes of the packed form of E matrices of
+ *   [N, K] (exactly E*N*K*9/16: no padding).  Returns 0 if the shape is unsupported.
+ *
+ * nvfp4_pack_weights: nib [E, N, K/2] canonical e2m1 bytes (row-major, even element in
+ *   the low nibble), scl [E, N, K/16] e4m3 scale bytes (row-major) -> packed
+ *   [nvfp4_packed_weight_bytes(E, N, K)] bytes, 16-byte aligned.  Values are unchanged:
+ *   it is a byte permutation.  Because the packed form is a sequence of independent
+ *   16-row tiles, packing a fused [2I, K] gate|up matrix gives the concatenation of the
+ *   packed gate and up matrices whenever I % 16 == 0.
+ *   Limits: N % 16 == 0, K % 128 == 0, E >= 1.
+ *
+ * nvfp4_unpack_weights: exact inverse of nvfp4_pack_weights (same limits).
+ * ---------------------------------------------------------------------------------- */
+size_t nvfp4_packed_weight_bytes(int E, int N, int K);
+int nvfp4_pack_weights(const uint8_t* nib, const uint8_t* scl, int E, int N, int K,
+                       void* packed, hipStream_t stream);
+int nvfp4_unpack_weights(const void* packed, int E, int N, int K,
+                         uint8_t* nib, uint8_t* scl, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * moe_gather_rows — group assignments by expert and gather their activation rows.
+ * Source: 2026-09-07 page, section "What changed": one row per (stream, expert) is
+ * gathered, and rows are grouped by expert id across the batch in ascending id order
+ * (an ordered map), so group order depends only on which experts fired.
+ *
+ * Inputs:  x [S, H] bf16; assignment j = (a_expert[j], a_src[j], a_dst[j], a_w[j]),
+ *          j < R: row a_src[j] of x goes to expert a_expert[j]; its result is added to
+ *          output row a_dst[j] (of T) with router weight a_w[j].
+ * Outputs: grouped row i (i < R) is the i-th assignment in (expert id, j) order.
+ *          expert_offsets [E+1]: rows of expert e are [expert_offsets[e],
+ *            expert_offsets[e+1]); expert_offsets[E] = number of valid rows Rv.
+ *          row_src, row_dst [R] int32, row_w [R] float: the assignment's fields.
+ *          tok_off [T+1], tok_rows [R]: token CSR — tok_rows[tok_off[t] ..
+ *            tok_off[t+1]) lists the grouped rows with row_dst == t, ascending.
+ *          xg [R, H] bf16: xg[i] = x[row_src[i]].
+ *          err_word (one int32): overwritten with the OR of MOE_ERR_* bits found.
+ *          Invalid assignments (expert, source or output row out of range) are
+ *          dropped: they fill rows [Rv, R) in ascending j with row_src = row_dst = -1,
+ *          row_w = 0 and a zero xg row, and are in no token's list.
+ * Limits:  R >= 0, S >= 0, 1 <= E <= 8192, 0 <= T, E + T <= 16000, H % 8 == 0.
+ * ---------------------------------------------------------------------------------- */
+int moe_gather_rows(const uint16_t* x, int S, int H,
+                    const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
+                    const float* a_w, int R, int E, int T,
+                    uint16_t* xg, int32_t* expert_offsets, int32_t* row_src,
+                    int32_t* row_dst, float* row_w, int32_t* tok_off, int32_t* tok_rows,
+                    int32_t* err_word, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * nvfp4_quantize_rows — NVFP4-quantize each bf16 row with its own fp32 global.
+ * Source: 2026-09-07 page, section "What changed" (the two quantize steps; the FP4
+ * tensor-core GEMM takes FP4 on both operands, section "Numbers").  The pages give no
+ * quantizer formula; this one is the two-level NVFP4 reading, in float32, in this order:
+ *   amax = max|x|; gs = amax / 2688 (1 if amax == 0)                 [2688 = 6 * 448]
+ *   per 16-block b: sf = max|x_b| / (6 * gs); sc[b] = e4m3fn(sf), nearest-even, saturating
+ *                   d = value(sc[b]) * gs
+ *   per element:    code = e2m1(x / d), nearest-even, saturating, sign kept; 0 if d == 0
+ * so that value = e2m1(code) * e4m3(sc[b]) * gs.  Output is bit-exact: every division
+ * is the correctly rounded IEEE one.
+ *
+ * in [R, K] bf16 -> q [R, K/2] (even element in the low nibble), sc [R, K/16],
+ * row_gs [R] float.  Limits: K % 16 == 0, 0 < K <= 8192, R >= 0; in 16-byte and q 8-byte
+ * aligned.
+ * ---------------------------------------------------------------------------------- */
+int nvfp4_quantize_rows(const uint16_t* in, int R, int K,
+                        uint8_t* q, uint8_t* sc, float* row_gs, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * grouped_gemm_nvfp4 — out[i, n] = sum_k a(i, k) * w_e(n, k) for every row i of every
+ * expert group e, with a = e2m1(aq) * e4m3(as) and w = e2m1 * e4m3 of expert e's packed
+ * weights; no globals (alpha = 1).
+ * Source: 2026-09-07 page, section "What changed": grouped GEMM w13 (N = 2I = 4096,
+ * K = H = 4096, fused gate|up) and w2 (N = H, K = I), alpha = 1.
+ *
+ * aq [R, K/2], as [R, K/16]: NVFP4 activation rows (as written by nvfp4_quantize_rows).
+ * expert_offsets [E+1] (device): groups as written by moe_gather_rows.
+ * w_packed: E experts of [N, K] packed by nvfp4_pack_weights.  out [R, N] float.
+ * Rows outside every group are not written.  Empty experts cost nothing.
+ * flags: MOE_PATH_*; gemv_max_rows: largest group taken by the GEMV path under
+ *   MOE_PATH_AUTO (0 = never).  Accumulation is fp32 in an order fixed by (N, K) and the
+ *   path alone, so a row's output does not depend on the other rows of its group.
+ * Limits: N % 16 == 0, K % 128 == 0, E <= 8192, 16-byte aligned pointers.
+ * ---------------------------------------------------------------------------------- */
+int grouped_gemm_nvfp4(const uint8_t* aq, const uint8_t* as, const int32_t* expert_offsets,
+                       int E, int R, const void* w_packed, int N, int K, float* out,
+                       int flags, int gemv_max_rows, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * swiglu_grouped — h[i, j] = bf16( silu(zg) * zu ), for row i of expert e:
+ *   zg = row_gs[i] * g_gate[e] * acc13[i, j],  zu = row_gs[i] * g_up[e] * acc13[i, I + j].
+ * Source: 2026-09-07 page, section "What changed" (per-group gate/up weight_scale_2
+ * applied in the SwiGLU kernel); 2026-09-06 page, section "Different globals on the two
+ * halves", option (a).  row_gs is the activation row global of the w13 GEMM's input.
+ *
+ * acc13 [R, 2I] float (gate in columns [0, I), up in [I, 2I)), expert_offsets [E+1],
+ * g_gate / g_up [E] float, row_gs [R] float -> h [R, I] bf16.  Rows outside every group
+ * are written as zeros.  Limits: I % 16 == 0, I <= 8192, E <= 8192.
+ * ---------------------------------------------------------------------------------- */
+int swiglu_grouped(const float* acc13, int R, int I, const int32_t* expert_offsets, int E,
+                   const float* g_gate, const float* g_up, const float* row_gs,
+                   uint16_t* h, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * moe_scatter_add — out[t] = bf16( sum over p in [tok_off[t], tok_off[t+1]), ascending,
+ *   of row_w[i] * g_down[e_i] * row_gs[i] * y[i] ),  i = tok_rows[p].
+ * Source: 2026-09-07 page, section "What changed" (scatter-add weighted by router weight
+ * * down weight_scale_2) and section "Proof" (shared accumulator row, accumulated in
+ * order of i).  row_gs is the activation row global of the w2 GEMM's input.
+ *
+ * y [R, H] float, expert_offsets [E+1], row_w [R], g_down [E], row_gs [R],
+ * tok_off [T+1], tok_rows -> out [T, H] bf16 (every row written; empty tokens are 0).
+ * Accumulation is fp32, in ascending p.  Limits: H % 4 == 0.
+ * ---------------------------------------------------------------------------------- */
+int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets, int E,
+                    const float* row_w, const float* g_down, const float* row_gs,
+                    const int32_t* tok_off, const int32_t* tok_rows, int T,
+                    uint16_t* out, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * moe_layer_forward — the whole routed-expert layer: every step above, in order, on
+ * one stream, with no host synchronization (2026-09-07 page, section "What changed").
+ * Gather is fused into the first quantize and SwiGLU into the second; the results are
+ * bit-identical to calling the separate entry points in sequence.
+ *
+ * L (host): E, H, I; w13_packed (E x [2I, H], gate rows first) and w2_packed
+ *   (E x [H, I]) from nvfp4_pack_weights; per-expert globals g_gate, g_up, g_down [E];
+ *   flags / gemv_max_rows as for grouped_gemm_nvfp4.
+ * x [S, H] bf16, assignments as for moe_gather_rows, out [T, H] bf16.
+ * workspace: >= moe_layer_workspace_bytes(L, S, R, T) bytes, 256-byte aligned.  Its
+ *   first int32 is the device error word (pass the workspace to moe_get_device_error).
+ * Limits: H % 128 == 0, I % 128 == 0, H and I <= 8192, plus those of the steps.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+  int E, H, I;
+  const void* w13_packed;
+  const void* w2_packed;
+  const float* g_gate;
+  const float* g_up;
+  const float* g_down;
+  int flags;
+  int gemv_max_rows;
+} moe_layer_desc;
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* L, int S, int R, int T);
+int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S,
+                      const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
+                      const float* a_w, int R, int T, uint16_t* out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Synchronizes `stream`, then returns the device error word at `err_word` (the
+ * err_word of moe_gather_rows, or a moe_layer_forward workspace), or a negative
+ * moe_status if the read fails. */
+int moe_get_device_error(const void* err_word, hipStream_t stream);
+
+/* Text of the last failure on the calling thread ("" if none).  Host pointer, valid
+ * until the thread's next call into the library. */
+const char* moe_last_error(void);
+
+/* Host string: hash of the sources this library was built from.  Bindings compare it
+ * with the sources on disk so that a stale build is refused instead of silently run
+ * (the 2026-09-07 page, section "A debugging note", lost a day to a stale test binary). */
+const char* moe_source_hash(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

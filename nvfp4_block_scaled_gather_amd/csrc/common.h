@@ -1,0 +1,134 @@
+// Shared device helpers and internal launch interfaces of the MoE NVFP4 library.
+// gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_nvfp4.h"
+
+namespace moe {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------------------ codec
+// e4m3fn value of a scale byte, as an exact float.  Normal codes: 2^(e-7) * (1 + m/8),
+// built directly as float bits; subnormal codes: m * 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                      : (float)m * 0.001953125f;
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// Nearest e4m3fn code of a non-negative float, ties to even, saturating at 448 (0x7E).
+// Normal range: round the float32 significand to 3 bits with round-half-even on the bit
+// pattern (a carry moves into the exponent); below 2^-6 the grid is uniform with step
+// 2^-9, so the code is rint(v * 512) (v * 512 is exact).
+__device__ __forceinline__ uint32_t e4m3_encode_pos(float v) {
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;  // biased exp : 3-bit mantissa
+  const uint32_t code = r - (120u << 3);                        // rebias 127 -> 7
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Nearest e2m1 code of a float, ties to even (code LSB 0), saturating at 6, sign kept.
+// Decision points are the midpoints of the grid {0, .5, 1, 1.5, 2, 3, 4, 6}; at a
+// midpoint the even code wins, which decides "<" versus "<=".
+__device__ __forceinline__ uint32_t e2m1_encode(float q) {
+  const float a = __builtin_fabsf(q);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return c | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+// bf16 <-> float
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------- dequantization
+// The gfx950 scaled FP4 conversion applies only the exponent of its fp32 scale operand,
+// so it cannot apply an e4m3 block scale (4 significant bits) by itself.  We convert
+// with a power-of-two scale of 2^8 and multiply by the block scale expressed as f16
+// times 2^-8: the e4m3fn byte with its exponent field re-read as f16 bits
+// ((b & 0x7F) << 7) is exactly e4m3 * 2^-8 for normal and subnormal codes alike.
+// Every product e2m1 * e4m3 (6 significant bits, magnitude in [2^-10, 2688]) is exact
+// in f16, so the dequantized operands are exact.
+__device__ __forceinline__ uint32_t e4m3_to_f16x2_scaled(uint32_t b) {
+  const uint32_t h = ((b & 0x7Fu) << 7) | ((b & 0x80u) << 8);
+  return h | (h << 16);
+}
+
+// Eight e2m1 nibbles (one 32-bit word, element 2k in the low nibble of byte k) times
+// the packed f16 scale pair -> 8 exact f16 values in element order.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, uint32_t scale_pair) {
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0);
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1);
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2);
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
+  const f16x2 s = __builtin_bit_cast(f16x2, scale_pair);
+  p0 *= s; p1 *= s; p2 *= s; p3 *= s;
+  f16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Eight e2m1 nibbles -> 8 exact f16 values of the bare e2m1 codes (no scale).
+__device__ __forceinline__ void e2m1x8_to_f16(uint32_t w, f16x2 out[4]) {
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+}
+
+// ------------------------------------------------------------------ packed weight layout
+// A matrix [N, K] is stored as N/16 tiles of 16 rows; a tile is K/128 chunks of 128
+// columns, and a chunk is 1152 contiguous bytes:
+//   [0, 1024):    lane l (0..63) owns bytes [16l, 16l + 16): row (l & 15) of the tile,
+//                 columns [128c + 32(l >> 4), +32) — the canonical nibble bytes of that
+//                 row segment, in order;
+//   [1024, 1152): lane l owns bytes [1024 + 2l, +2): the two e4m3 scale bytes of that
+//                 same 32-column row segment.
+// So one wave reads a tile's chunk with one 16-byte and one 2-byte load per lane, both
+// perfectly coalesced.  A tile is 9K bytes and an expert N/16 consecutive tiles; there
+// is no padding (N * K * 9/16 bytes per expert).
+constexpr int kChunkBytes = 1152;
+
+}  // namespace moe
+
+// ------------------------------------------------------------------ internal launchers
+// (host functions defined in the kernel translation units; arguments already validated)
+namespace moe {
+hipError_t launch_pack(const uint8_t* nib, const uint8_t* scl, int E, int N, int K, uint8_t* packed,
+                       bool unpack, uint8_t* nib_out, uint8_t* scl_out, hipStream_t s);
+hipError_t launch_group(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
+                        const float* a_w, int R, int E, int S, int T, int32_t* expert_offsets,
+                        int32_t* row_src, int32_t* row_dst, float* row_w, int32_t* tok_off,
+                        int32_t* tok_rows, int32_t* err_word, hipStream_t s);
+hipError_t launch_gather(const uint16_t* x, int H, const int32_t* row_src, int R, uint16_t* xg,
+                         hipStream_t s);
+hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, int R, int K, uint8_t* q,
+                           uint8_t* sc, float* row_gs, hipStream_t s);
+hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* expert_offsets, int E,
+                         const float* g_gate, const float* g_up, const float* row_gs,
+                         uint16_t* h, uint8_t* q, uint8_t* sc, float* h_gs, hipStream_t s);
+hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* expert_offsets,
+                               int E, int R, const uint8_t* w, int N, int K, float* out,
+                               int flags, int gemv_max_rows, hipStream_t s);
+hipError_t launch_scatter(const float* y, int R, int H, const int32_t* expert_offsets, int E,
+                          const float* row_w, const float* g_down, const float* row_gs,
+                          const int32_t* tok_off, const int32_t* tok_rows, int T, uint16_t* out,
+                          hipStream_t s);
+}  // namespace moe

@@ -15,7 +15,9 @@ and real prompts that are not available; these stand in for them):
 * ``zipf512``: 64 tokens, top-8 over 288 experts with Zipf(1.1) popularity.
 
 Weights for expert e and tensor t come from a counter-based Philox stream keyed by
-(seed, e, t), so any expert can be regenerated alone.
+(weight_seed, e, t), so any expert can be regenerated alone.  The four full-size workloads
+share one weight seed (one resident expert set serves all of them); routing and
+activations have a seed per workload.
 """
 import dataclasses
 
@@ -100,16 +102,17 @@ class Workload:
     g_up: np.ndarray
     g_down: np.ndarray
     seed: int
+    weight_seed: int
 
     @property
     def R(self):
         return len(self.a_expert)
 
     def w13(self, e):
-        return expert_weights(self.seed, e, TENSOR_W13, 2 * self.I, self.H)
+        return expert_weights(self.weight_seed, e, TENSOR_W13, 2 * self.I, self.H)
 
     def w2(self, e):
-        return expert_weights(self.seed, e, TENSOR_W2, self.H, self.I)
+        return expert_weights(self.weight_seed, e, TENSOR_W2, self.H, self.I)
 
     def active_experts(self):
         return sorted(set(int(e) for e in self.a_expert if 0 <= e < self.E))
@@ -129,11 +132,12 @@ def _ragged_counts(g, R, E):
     return 1 + g.multinomial(R - E, np.full(E, 1.0 / E))
 
 
-def make_workload(name, seed=None, E=None, H=None, I=None):
+def make_workload(name, seed=None, E=None, H=None, I=None, weight_seed=None):
     """Build one of the named workloads.  E/H/I override the full dims (tests use
     smaller shapes with the same structure)."""
     idx = WORKLOADS.index(name)
     seed = BASE_SEED + idx if seed is None else seed
+    weight_seed = BASE_SEED if weight_seed is None else weight_seed
     full = dict(E=288, H=4096, I=2048)
     if name == "tiny":
         full = dict(E=8, H=256, I=128)
@@ -204,4 +208,4 @@ def make_workload(name, seed=None, E=None, H=None, I=None):
                     a_src=a_src.astype(np.int32), a_dst=a_dst.astype(np.int32),
                     a_w=a_w.astype(np.float32),
                     g_gate=np.full(E, G_GATE, np.float32), g_up=np.full(E, G_UP, np.float32),
-                    g_down=np.full(E, G_DOWN, np.float32), seed=seed)
+                    g_down=np.full(E, G_DOWN, np.float32), seed=seed, weight_seed=weight_seed)

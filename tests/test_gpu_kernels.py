@@ -1,0 +1,381 @@
+"""GPU parity of each library entry point against the CPU oracle, through the C ABI.
+
+Bit-exact: weight packing, grouping / gather indices, quantized nibbles / scale bytes /
+row globals, and GEMMs whose every partial sum is exact.  Tolerances elsewhere:
+GEMM max |gpu - oracle| <= 2e-3 x row RMS (fp32 accumulation vs float64 over identical
+exact operands); SwiGLU and scatter within one bf16 rounding step.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe as omoe
+from oracle import nvfp4 as onv
+
+from gpu_helpers import dev, empty, host, offsets_from_sizes, pack, rand_nvfp4, run_gemm, say, sync
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 2e-3
+
+
+# ------------------------------------------------------------------------------ packing
+def test_pack_unpack_roundtrip_and_fused_concat(lib):
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    rng = np.random.default_rng(1)
+    for (E, N, K) in [(3, 48, 384), (2, 32, 4096), (1, 16, 128)]:
+        say("pack", E, N, K)
+        nib, scl = rand_nvfp4(rng, E * N, K, 0, 255)
+        wp = pack(B, nib, scl, E, N, K)
+        assert wp.numel() == E * N * K * 9 // 16
+        nib2 = empty((E * N, K // 2), torch.uint8)
+        scl2 = empty((E * N, K // 16), torch.uint8)
+        B.nvfp4_unpack_weights(wp, E, N, K, nib2, scl2)
+        sync()
+        assert np.array_equal(host(nib2), nib) and np.array_equal(host(scl2), scl)
+    # fused gate|up packs to the concatenation of the separately packed halves
+    I, K = 32, 256
+    g, gs = rand_nvfp4(rng, I, K, 0, 255)
+    u, us = rand_nvfp4(rng, I, K, 0, 255)
+    fused = host(pack(B, np.concatenate([g, u]), np.concatenate([gs, us]), 1, 2 * I, K))
+    sep = np.concatenate([host(pack(B, g, gs, 1, I, K)), host(pack(B, u, us, 1, I, K))])
+    assert np.array_equal(fused, sep)
+
+
+# ------------------------------------------------------------------------------ quantize
+def _special_rows(K):
+    rows = []
+    rows.append(np.zeros(K, np.float32))
+    x = np.zeros(K, np.float32)
+    x[:16] = np.arange(1, 17)
+    rows.append(x)
+    x = np.zeros(K, np.float32)
+    x[:16] = np.arange(-8, 8)
+    rows.append(x)
+    x = np.zeros(K, np.float32)
+    x[:16] = [6, 3, 1.5, 0.75, 0.375, 0.1875, 0, -6, -3, -1.5, -0.75, -0.375, -0.1875, -0.0, 0.25, 2.5]
+    rows.append(x)
+    x = np.full(K, -0.0, np.float32)
+    x[5] = 1.0
+    rows.append(x)
+    rng = np.random.default_rng(9)
+    rows.append((rng.standard_normal(K) * 1e-39).astype(np.float32))    # bf16 subnormal range
+    rows.append((rng.standard_normal(K) * 1e37).astype(np.float32))     # near the top
+    x = (rng.standard_normal(K) * np.exp(rng.uniform(-12, 12, K))).astype(np.float32)
+    rows.append(x)                                                     # blocks of every size
+    x = rng.standard_normal(K).astype(np.float32)
+    x[::16] = 0
+    x[K // 2:K // 2 + 16] = 2.0 ** -30                                 # underflowing block scale
+    rows.append(x)
+    return np.stack(rows)
+
+
+def _to_bf16_bits(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("K,R", [(64, 131), (16, 5), (256, 40), (2048, 24), (4096, 24), (8192, 4)])
+def test_quantize_bit_exact(lib, K, R):
+    """K=64 with 131 rows is the shape of the page's kernel check (groups of 1 and 130
+    rows, 2026-09-07 page, section "Proof")."""
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("quantize K=%d R=%d" % (K, R))
+    rng = np.random.default_rng(K + R)
+    x = (rng.standard_normal((R, K)) * np.exp(rng.uniform(-3, 3, (R, 1)))).astype(np.float32)
+    if K >= 16:
+        x = np.concatenate([x, _special_rows(K)])
+    bits = _to_bf16_bits(x)
+    R = bits.shape[0]
+    q = empty((R, K // 2), torch.uint8)
+    sc = empty((R, K // 16), torch.uint8)
+    gs = empty((R,), torch.float32)
+    B.nvfp4_quantize_rows(dev(bits), R, K, q, sc, gs)
+    sync()
+    wq, ws, wg = onv.quantize_rows(onv.bf16_bits_to_f32(bits))
+    assert np.array_equal(host(q), wq)
+    assert np.array_equal(host(sc), ws)
+    assert np.array_equal(host(gs).view(np.uint32), wg.view(np.uint32))
+
+
+def test_quantize_empty_batch(lib):
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    B.nvfp4_quantize_rows(empty((1, 64), torch.int16), 0, 64, empty((1, 32), torch.uint8),
+                          empty((1, 4), torch.uint8), empty((1,), torch.float32))
+    sync()
+
+
+# ------------------------------------------------------------------------------ group / gather
+def _run_group(B, x, S, H, a_expert, a_src, a_dst, a_w, E, T):
+    import torch
+    R = len(a_expert)
+    Rb = max(R, 1)
+    outs = dict(xg=empty((Rb, H), torch.int16), offsets=empty((E + 1,), torch.int32),
+                row_src=empty((Rb,), torch.int32), row_dst=empty((Rb,), torch.int32),
+                row_w=empty((Rb,), torch.float32), tok_off=empty((T + 1,), torch.int32),
+                tok_rows=empty((Rb,), torch.int32), err=empty((1,), torch.int32))
+    B.moe_gather_rows(dev(x) if S else empty((1, H), torch.int16), S, H, dev(a_expert),
+                      dev(a_src), dev(a_dst), dev(a_w), R, E, T, outs["xg"], outs["offsets"],
+                      outs["row_src"], outs["row_dst"], outs["row_w"], outs["tok_off"],
+                      outs["tok_rows"], outs["err"])
+    err = B.moe_get_device_error(outs["err"])
+    return {k: host(v) for k, v in outs.items()}, err
+
+
+@pytest.mark.parametrize("case", ["random_invalid", "ragged570", "zipf", "empty", "one_expert"])
+def test_group_gather_bit_exact(lib, case):
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("group", case)
+    rng = np.random.default_rng(sum(map(ord, case)))
+    H = 64
+    if case == "random_invalid":
+        E, S, T, R = 13, 20, 9, 300
+        a_expert = rng.integers(-2, E + 2, R)
+        a_src = rng.integers(-1, S + 1, R)
+        a_dst = rng.integers(-1, T + 1, R)
+    elif case == "ragged570":
+        E, S, T, R = 288, 570, 8, 570
+        a_expert = np.repeat(np.arange(E), 1 + rng.multinomial(R - E, np.full(E, 1 / E)))
+        a_src = np.arange(R)
+        a_dst = rng.integers(0, T, R)
+    elif case == "zipf":
+        E, S, T = 288, 64, 64
+        p = (rng.permutation(E) + 1.0) ** -1.1
+        a_expert = np.concatenate([rng.choice(E, 8, replace=False, p=p / p.sum()) for _ in range(T)])
+        a_src = np.repeat(np.arange(T), 8)
+        a_dst = a_src.copy()
+        R = len(a_expert)
+    elif case == "empty":
+        E, S, T, R = 8, 4, 4, 0
+        a_expert = a_src = a_dst = np.zeros(0, np.int64)
+    else:
+        E, S, T, R = 5, 3, 2, 100
+        a_expert = np.full(R, 3)
+        a_src = rng.integers(0, S, R)
+        a_dst = rng.integers(0, T, R)
+    a_w = rng.random(R).astype(np.float32)
+    x = rng.integers(0, 65536, (max(S, 1), H)).astype(np.uint16)[:S]
+    a_expert, a_src, a_dst = (np.asarray(v, np.int32) for v in (a_expert, a_src, a_dst))
+    got, err = _run_group(B, x, S, H, a_expert, a_src, a_dst, a_w, E, T)
+    want = omoe.group_rows(a_expert, a_src, a_dst, a_w, E, S, T)
+    assert err == want["err"]
+    assert np.array_equal(got["offsets"], want["offsets"])
+    assert np.array_equal(got["tok_off"], want["tok_off"])
+    if R:
+        assert np.array_equal(got["row_src"][:R], want["row_src"])
+        assert np.array_equal(got["row_dst"][:R], want["row_dst"])
+        assert np.array_equal(got["row_w"][:R].view(np.uint32), want["row_w"].view(np.uint32))
+        Rv = int(want["offsets"][E])
+        assert np.array_equal(got["tok_rows"][:Rv], want["tok_rows"])
+        xg = omoe.gather_rows(x, want["row_src"])
+        assert np.array_equal(got["xg"][:R].view(np.uint16), xg)
+
+
+# ------------------------------------------------------------------------------ GEMM
+def _oracle_gemm(aq, as_, offsets, wnib, wscl, E, N, K):
+    return omoe.grouped_gemm(aq, as_, offsets,
+                             lambda e: (wnib[e * N:(e + 1) * N], wscl[e * N:(e + 1) * N]), N, K)
+
+
+SIZES = [1, 2, 0, 3, 4, 5, 16, 17, 33, 8, 0, 1]
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2])
+def test_gemm_exact_arithmetic_bit_exact(lib, flags):
+    """All scales 1.0: every product is a multiple of 1/4 and every partial sum over
+    K = 4096 is exact in fp32, so any summation order gives the oracle's value exactly."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm exact flags", flags)
+    rng = np.random.default_rng(20 + flags)
+    N, K = 256, 4096
+    E = len(SIZES)
+    offsets = offsets_from_sizes(SIZES)
+    R = int(offsets[-1])
+    aq, as_ = rand_nvfp4(rng, R, K, 0x38, 0x38)
+    wn, ws = rand_nvfp4(rng, E * N, K, 0x38, 0x38)
+    wp = pack(B, wn, ws, E, N, K)
+    got = run_gemm(B, aq, as_, offsets, wp, N, K, flags)
+    want = _oracle_gemm(aq, as_, offsets, wn, ws, E, N, K)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_gemm_one_hot_activations_read_back_every_weight(lib, flags):
+    """One-hot activation rows (a single 1.0) turn the GEMM into a read-back of the
+    dequantized weights: exact for every e2m1 code times every finite e4m3 scale code."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm one-hot activations flags", flags)
+    rng = np.random.default_rng(30 + flags)
+    N, K = 64, 256
+    codes = np.zeros((K, K), np.uint8)
+    codes[np.arange(K), np.arange(K)] = 2                  # 1.0
+    aq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    as_ = np.full((K, K // 16), 0x38, np.uint8)
+    wn = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    ws = finite[rng.integers(0, len(finite), (N, K // 16))]
+    ws[:16, :] = np.resize(finite, 16 * (K // 16)).reshape(16, K // 16)  # every code appears
+    wp = pack(B, wn, ws, 1, N, K)
+    offsets = np.array([0, K], np.int32)
+    got = run_gemm(B, aq, as_, offsets, wp, N, K, flags)
+    want = onv.dequantize(wn, ws).T                        # [K, N]
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_gemm_one_hot_weights_read_back_every_activation(lib, flags):
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm one-hot weights flags", flags)
+    rng = np.random.default_rng(40 + flags)
+    N = K = 128
+    perm = rng.permutation(K)
+    codes = np.zeros((N, K), np.uint8)
+    codes[np.arange(N), perm] = 2
+    wn = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    ws = np.full((N, K // 16), 0x38, np.uint8)
+    wp = pack(B, wn, ws, 1, N, K)
+    finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+    R = 21
+    aq = rng.integers(0, 256, (R, K // 2)).astype(np.uint8)
+    as_ = finite[rng.integers(0, len(finite), (R, K // 16))]
+    got = run_gemm(B, aq, as_, np.array([0, R], np.int32), wp, N, K, flags)
+    want = onv.dequantize(aq, as_)[:, perm]
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def _workload_like(rng, R, K):
+    """Activation rows quantized by the oracle from bf16 N(0,1); weights as in the bench."""
+    x = _to_bf16_bits(rng.standard_normal((R, K)).astype(np.float32))
+    aq, as_, _ = onv.quantize_rows(onv.bf16_bits_to_f32(x))
+    return aq, as_
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2])
+def test_gemm_random_within_tolerance(lib, flags):
+    from nvfp4_block_scaled_gather_amd import binding as B
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("gemm random flags", flags)
+    rng = np.random.default_rng(50 + flags)
+    N, K = 512, 4096
+    sizes = [1, 3, 0, 4, 5, 7, 16, 18, 40, 2]
+    E = len(sizes)
+    offsets = offsets_from_sizes(sizes)
+    R = int(offsets[-1])
+    aq, as_ = _workload_like(rng, R, K)
+    ws_ = [W.expert_weights(77, e, 0, N, K) for e in range(E)]
+    wn = np.concatenate([w[0] for w in ws_])
+    wsc = np.concatenate([w[1] for w in ws_])
+    wp = pack(B, wn, wsc, E, N, K)
+    got = run_gemm(B, aq, as_, offsets, wp, N, K, flags)
+    want = _oracle_gemm(aq, as_, offsets, wn, wsc, E, N, K)
+    rms = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True))
+    err = np.abs(got - want)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= GEMM_TOL * rms), float((err / rms).max())
+
+
+@pytest.mark.parametrize("flags,sizes", [(1, [1, 2, 3, 4]), (2, [1, 5, 8, 16, 17, 33])])
+def test_gemm_row_invariance_within_path(lib, flags, sizes):
+    """2026-09-07 page, section "Proof": a row's output is the same alone or grouped."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm row invariance", flags, sizes)
+    rng = np.random.default_rng(60 + flags)
+    N, K = 128, 2048
+    aq, as_ = _workload_like(rng, max(sizes), K)
+    wn, wsc = rand_nvfp4(rng, N, K, 0x20, 0x40)
+    wp = pack(B, wn, wsc, 1, N, K)
+    alone = np.concatenate([run_gemm(B, aq[i:i + 1], as_[i:i + 1], np.array([0, 1], np.int32), wp,
+                                     N, K, flags) for i in range(max(sizes))])
+    for g in sizes:
+        grouped = run_gemm(B, aq[:g], as_[:g], np.array([0, g], np.int32), wp, N, K, flags)
+        assert np.array_equal(grouped.view(np.uint32), alone[:g].view(np.uint32)), g
+
+
+@pytest.mark.parametrize("flags", [1, 2])
+def test_gemm_fused_w13_equals_separate_and_is_deterministic(lib, flags):
+    """2026-09-07 page, section "Proof": fused gate|up == gate-only and up-only GEMMs,
+    and five repeated calls are bit-identical."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm fused/determinism", flags)
+    rng = np.random.default_rng(70 + flags)
+    I, K = 256, 1024
+    sizes = [3, 6, 20]
+    offsets = offsets_from_sizes(sizes)
+    R = int(offsets[-1])
+    E = len(sizes)
+    aq, as_ = _workload_like(rng, R, K)
+    gate = [rand_nvfp4(rng, I, K, 0x20, 0x40) for _ in range(E)]
+    up = [rand_nvfp4(rng, I, K, 0x20, 0x40) for _ in range(E)]
+    fn = np.concatenate([np.concatenate([g[0], u[0]]) for g, u in zip(gate, up)])
+    fs = np.concatenate([np.concatenate([g[1], u[1]]) for g, u in zip(gate, up)])
+    fused = run_gemm(B, aq, as_, offsets, pack(B, fn, fs, E, 2 * I, K), 2 * I, K, flags)
+    g_only = run_gemm(B, aq, as_, offsets, pack(B, np.concatenate([g[0] for g in gate]),
+                                                 np.concatenate([g[1] for g in gate]), E, I, K),
+                      I, K, flags)
+    u_only = run_gemm(B, aq, as_, offsets, pack(B, np.concatenate([u[0] for u in up]),
+                                                 np.concatenate([u[1] for u in up]), E, I, K),
+                      I, K, flags)
+    assert np.array_equal(fused[:, :I].view(np.uint32), g_only.view(np.uint32))
+    assert np.array_equal(fused[:, I:].view(np.uint32), u_only.view(np.uint32))
+    wp = pack(B, fn, fs, E, 2 * I, K)
+    for _ in range(5):
+        again = run_gemm(B, aq, as_, offsets, wp, 2 * I, K, flags)
+        assert np.array_equal(again.view(np.uint32), fused.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------ SwiGLU
+def test_swiglu_within_one_bf16_step(lib):
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("swiglu")
+    rng = np.random.default_rng(80)
+    I, E = 2048, 6
+    sizes = [3, 0, 5, 1, 0, 7]
+    offsets = offsets_from_sizes(sizes)
+    R = int(offsets[-1]) + 2                      # two rows outside every group
+    acc = (rng.standard_normal((R, 2 * I)) * 40000).astype(np.float32)
+    gs = (rng.uniform(0.5, 2, R) * 1e-3).astype(np.float32)
+    g_gate = (rng.uniform(0.5, 2, E) * 4.65e-2).astype(np.float32)
+    g_up = (rng.uniform(0.5, 2, E) * 3.78e-2).astype(np.float32)
+    h = empty((R, I), torch.int16)
+    B.swiglu_grouped(dev(acc), R, I, dev(offsets), E, dev(g_gate), dev(g_up), dev(gs), h)
+    sync()
+    got = onv.bf16_bits_to_f32(host(h).view(np.uint16)).astype(np.float64)
+    want = onv.bf16_bits_to_f32(omoe.swiglu(acc.astype(np.float64), offsets, g_gate, g_up, gs, I))
+    want = want.astype(np.float64)
+    ulp = np.abs(want) * 2.0 ** -7 + 1e-38
+    assert np.all(np.abs(got - want) <= ulp)
+    assert np.mean(got == want) > 0.98
+    assert not got[offsets[-1]:].any()
+
+
+# ------------------------------------------------------------------------------ scatter
+def test_scatter_within_bf16_rounding(lib):
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("scatter")
+    rng = np.random.default_rng(90)
+    E, H, T = 7, 4096, 9
+    sizes = [4, 0, 9, 2, 30, 1, 3]
+    offsets = offsets_from_sizes(sizes)
+    R = int(offsets[-1])
+    a_dst = rng.integers(0, T - 1, R).astype(np.int32)     # token T-1 gets no rows
+    a_expert = np.repeat(np.arange(E), sizes).astype(np.int32)
+    g = omoe.group_rows(a_expert, np.zeros(R, np.int32), a_dst, np.ones(R, np.float32), E, 1, T)
+    y = (rng.standard_normal((R, H)) * 1e5).astype(np.float32)
+    row_w = rng.random(R).astype(np.float32)
+    g_down = (rng.uniform(0.5, 2, E) * 4.2e-5).astype(np.float32)
+    gs = (rng.uniform(0.5, 2, R) * 1e-8).astype(np.float32)
+    out = empty((T, H), torch.int16)
+    B.moe_scatter_add(dev(y), R, H, dev(offsets), E, dev(row_w), dev(g_down), dev(gs),
+                      dev(g["tok_off"]), dev(g["tok_rows"]), T, out)
+    sync()
+    got = onv.bf16_bits_to_f32(host(out).view(np.uint16)).astype(np.float64)
+    want = onv.bf16_bits_to_f32(omoe.scatter_add(y.astype(np.float64), offsets, row_w, g_down, gs,
+                                                 g["tok_off"], g["tok_rows"], T)).astype(np.float64)
+    scale = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True)) + 1e-30
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-5 * scale)
+    assert not got[T - 1].any()

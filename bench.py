@@ -49,7 +49,25 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-experts", type=int, default=24,
                    help="experts in the oracle's bounded sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy 3 times (reference for the HBM "
+                        "byte counters) and exit")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of known size, so that profiler byte counters
+    (FETCH_SIZE, WRITE_SIZE) can be scaled: each copy reads and writes 1 GiB."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": 3}), flush=True)
 
 
 def time_layer(dl, steps, warmup):
@@ -190,6 +208,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     from nvfp4_block_scaled_gather_amd import binding as B
     B.load()
     wl, dl, res, weights = run_workload(args.workload, args)

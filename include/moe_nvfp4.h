@@ -172,15 +172,17 @@ int swiglu_grouped(const float* acc13, int R, int I, const int32_t* expert_offse
                    uint16_t* h, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------------
- * moe_scatter_add — out[t] = bf16( sum over p in [tok_off[t], tok_off[t+1]), ascending,
- *   of row_w[i] * g_down[e_i] * row_gs[i] * y[i] ),  i = tok_rows[p].
+ * moe_scatter_add — out[t] = bf16( sum over p in [tok_off[t], tok_off[t+1]) of
+ *   row_w[i] * g_down[e_i] * row_gs[i] * y[i] ),  i = tok_rows[p].
  * Source: 2026-09-07 page, section "What changed" (scatter-add weighted by router weight
  * * down weight_scale_2) and section "Proof" (shared accumulator row, accumulated in
  * order of i).  row_gs is the activation row global of the w2 GEMM's input.
  *
  * y [R, H] float, expert_offsets [E+1], row_w [R], g_down [E], row_gs [R],
  * tok_off [T+1], tok_rows -> out [T, H] bf16 (every row written; empty tokens are 0).
- * Accumulation is fp32, in ascending p.  Limits: H % 4 == 0.
+ * Accumulation is fp32 in a fixed order that depends only on the token's row count
+ * (eight interleaved ascending partial sums, added in order), so a token's output does
+ * not depend on the rest of the batch.  Limits: H % 4 == 0.
  * ---------------------------------------------------------------------------------- */
 int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets, int E,
                     const float* row_w, const float* g_down, const float* row_gs,
@@ -190,8 +192,11 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
 /* ----------------------------------------------------------------------------------
  * moe_layer_forward — the whole routed-expert layer: every step above, in order, on
  * one stream, with no host synchronization (2026-09-07 page, section "What changed").
- * Gather is fused into the first quantize and SwiGLU into the second; the results are
- * bit-identical to calling the separate entry points in sequence.
+ * The S source rows are quantized once each, in the same launch as the grouping, and the
+ * w13 GEMM reads grouped row i from source row row_src[i] (a row's codes depend only on
+ * the row, so this equals gather-then-quantize); the second quantize is fused into
+ * SwiGLU.  The results are bit-identical to calling the separate entry points in
+ * sequence.
  *
  * L (host): E, H, I; w13_packed (E x [2I, H], gate rows first) and w2_packed
  *   (E x [H, I]) from nvfp4_pack_weights; per-expert globals g_gate, g_up, g_down [E];

@@ -24,8 +24,10 @@ MOE_ERR_EXPERT = 1
 MOE_ERR_SRC = 2
 MOE_ERR_DST = 4
 
-# Default largest group on the GEMV path under MOE_PATH_AUTO.
-DEFAULT_GEMV_MAX_ROWS = 4
+# Default largest group on the GEMV path under MOE_PATH_AUTO.  Measured on MI355X, the MFMA
+# path streams the weights faster than the GEMV path for every group size, one row included,
+# so by default every group takes the MFMA path; the GEMV path stays selectable.
+DEFAULT_GEMV_MAX_ROWS = 0
 
 
 class MoeError(RuntimeError):

@@ -148,8 +148,11 @@ int grouped_gemm_nvfp4(const uint8_t* aq, const uint8_t* as, const int32_t* expe
                        int gemv_max_rows, hipStream_t stream) {
   int st = check_gemm_args(aq, as, expert_offsets, E, R, w_packed, N, K, out, flags, gemv_max_rows);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_grouped_gemm(aq, as, expert_offsets, E, R, (const uint8_t*)w_packed,
-                                             N, K, out, flags, gemv_max_rows, stream),
+  REQUIRE((long long)R * (K / 2) < (1ll << 31), MOE_EUNSUPPORTED,
+          "grouped GEMM: activations of %d rows x %d columns exceed 2 GiB", R, K);
+  return hip_status(moe::launch_grouped_gemm(aq, as, nullptr, R, expert_offsets, E,
+                                             (const uint8_t*)w_packed, N, K, out, flags,
+                                             gemv_max_rows, stream),
                     "grouped GEMM launch");
 }
 
@@ -163,8 +166,8 @@ int swiglu_grouped(const float* acc13, int R, int I, const int32_t* expert_offse
   REQUIRE(expert_offsets && g_gate && g_up, MOE_EINVAL, "swiglu: null offsets / globals");
   if (R > 0) REQUIRE(acc13 && row_gs && h, MOE_EINVAL, "swiglu: null pointer");
   REQUIRE(aligned(acc13, 16) && aligned(h, 16), MOE_EINVAL, "swiglu: acc13 / h not 16-byte aligned");
-  return hip_status(moe::launch_swiglu(acc13, R, I, expert_offsets, E, g_gate, g_up, row_gs, h,
-                                       nullptr, nullptr, nullptr, stream),
+  return hip_status(moe::launch_swiglu(acc13, R, I, expert_offsets, E, g_gate, g_up, row_gs, nullptr,
+                                       h, nullptr, nullptr, nullptr, stream),
                     "swiglu launch");
 }
 
@@ -205,7 +208,6 @@ struct LayerWs {
 };
 
 LayerWs carve(const moe_layer_desc* L, int S, int R, int T, uint8_t* base) {
-  (void)S;
   LayerWs w{};
   size_t o = 0;
   auto take = [&](size_t n) {
@@ -221,9 +223,10 @@ LayerWs carve(const moe_layer_desc* L, int S, int R, int T, uint8_t* base) {
   w.row_w = (float*)take(4 * r);
   w.tok_off = (int32_t*)take(4 * ((size_t)T + 1));
   w.tok_rows = (int32_t*)take(4 * r);
-  w.xq = take(r * L->H / 2);
-  w.xs = take(r * L->H / 16);
-  w.xgs = (float*)take(4 * r);
+  const size_t sr = (size_t)S;  // x is quantized once per source row
+  w.xq = take(sr * L->H / 2);
+  w.xs = take(sr * L->H / 16);
+  w.xgs = (float*)take(4 * sr);
   const size_t acc_cols = (size_t)(2 * L->I > L->H ? 2 * L->I : L->H);
   w.acc = (float*)take(4 * r * acc_cols);
   w.hq = take(r * L->I / 2);
@@ -242,6 +245,8 @@ int check_layer(const moe_layer_desc* L, int S, int R, int T) {
   REQUIRE(L->I > 0 && L->I % 128 == 0 && L->I <= kMaxRowK, MOE_EUNSUPPORTED,
           "layer: I=%d must be a multiple of 128 in (0, %d]", L->I, kMaxRowK);
   REQUIRE(L->E + T <= kMaxGroupKeys, MOE_EUNSUPPORTED, "layer: E + T exceeds %d", kMaxGroupKeys);
+  REQUIRE((long long)(S > R ? S : R) * L->H < (1ll << 31), MOE_EUNSUPPORTED,
+          "layer: activations exceed 2 GiB of NVFP4 rows");
   return MOE_OK;
 }
 }  // namespace
@@ -272,22 +277,23 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
   REQUIRE(L->gemv_max_rows >= 0, MOE_EINVAL, "layer: gemv_max_rows < 0");
   const int E = L->E, H = L->H, I = L->I;
   hipError_t e;
-  e = moe::launch_group(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src, w.row_dst,
-                        w.row_w, w.tok_off, w.tok_rows, w.err, stream);
-  if (e != hipSuccess) return hip_status(e, "layer: group launch");
-  e = moe::launch_quantize(x, w.row_src, R, H, w.xq, w.xs, w.xgs, stream);
-  if (e != hipSuccess) return hip_status(e, "layer: gather+quantize launch");
+  // grouping + NVFP4 quantization of the S source rows (one launch); the w13 GEMM reads
+  // grouped row i from source row row_src[i], so no gathered copy of x is made
+  e = moe::launch_group_quantize(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
+                                 w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, x, H, w.xq, w.xs,
+                                 w.xgs, stream);
+  if (e != hipSuccess) return hip_status(e, "layer: group+quantize launch");
   if (R > 0) {
-    e = moe::launch_grouped_gemm(w.xq, w.xs, w.offsets, E, R, (const uint8_t*)L->w13_packed, 2 * I, H,
-                                 w.acc, L->flags, L->gemv_max_rows, stream);
+    e = moe::launch_grouped_gemm(w.xq, w.xs, w.row_src, S, w.offsets, E, (const uint8_t*)L->w13_packed,
+                                 2 * I, H, w.acc, L->flags, L->gemv_max_rows, stream);
     if (e != hipSuccess) return hip_status(e, "layer: w13 GEMM launch");
   }
-  e = moe::launch_swiglu(w.acc, R, I, w.offsets, E, L->g_gate, L->g_up, w.xgs, nullptr, w.hq, w.hs,
-                         w.hgs, stream);
+  e = moe::launch_swiglu(w.acc, R, I, w.offsets, E, L->g_gate, L->g_up, w.xgs, w.row_src, nullptr,
+                         w.hq, w.hs, w.hgs, stream);
   if (e != hipSuccess) return hip_status(e, "layer: swiglu+quantize launch");
   if (R > 0) {
-    e = moe::launch_grouped_gemm(w.hq, w.hs, w.offsets, E, R, (const uint8_t*)L->w2_packed, H, I, w.acc,
-                                 L->flags, L->gemv_max_rows, stream);
+    e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, R, w.offsets, E, (const uint8_t*)L->w2_packed, H,
+                                 I, w.acc, L->flags, L->gemv_max_rows, stream);
     if (e != hipSuccess) return hip_status(e, "layer: w2 GEMM launch");
   }
   e = moe::launch_scatter(w.acc, R, H, w.offsets, E, w.row_w, L->g_down, w.hgs, w.tok_off, w.tok_rows,

@@ -106,6 +106,89 @@ __device__ __forceinline__ void e2m1x8_to_f16(uint32_t w, f16x2 out[4]) {
 // is no padding (N * K * 9/16 bytes per expert).
 constexpr int kChunkBytes = 1152;
 
+// ------------------------------------------------------------------ row quantization
+__device__ __forceinline__ float wave_max(float v) {
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+  return v;
+}
+
+// Expand 16 bf16 values (two 16-byte words, element order) to floats.
+__device__ __forceinline__ void bf16x16_to_f32(const u32x4& w0, const u32x4& w1, float* v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w0[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w0[e] & 0xFFFF0000u);
+    v[8 + 2 * e] = __uint_as_float(w1[e] << 16);
+    v[8 + 2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
+  }
+}
+
+// NVFP4 row quantization, for a row held by `nthreads` threads of the workgroup (a
+// multiple of 64, aligned to a wave): thread t (0 <= t < nthreads) owns scale blocks
+// b = t + nthreads * k (k < BPT, b < NB) and holds their 16 values in v[k][.].
+// Arithmetic, in float32 with correctly rounded divisions and no contraction, in order:
+//   amax = max|x|; gs = amax / 2688 (1 if amax == 0); per block: sf = max|x_b| / (6 gs),
+//   sc = e4m3(sf) nearest-even saturating, d = e4m3_value(sc) * gs; per element:
+//   code = e2m1(x / d) nearest-even saturating with its sign, 0 if d == 0.
+//
+// Step 1: the row's amax.  Every thread of the workgroup must call this together (it has a
+// workgroup barrier).  s_red: nthreads / 64 floats of LDS private to this row.
+template <int BPT>
+__device__ __forceinline__ float row_amax_threads(const float (&v)[BPT][16], int t, int nthreads,
+                                                  float* s_red) {
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, __builtin_fabsf(v[k][e]));
+  m = wave_max(m);
+  if ((t & 63) == 0) s_red[t >> 6] = m;
+  __syncthreads();
+  float amax = 0.0f;
+  for (int w = 0; w < nthreads / 64; ++w) amax = fmaxf(amax, s_red[w]);
+  return amax;
+}
+
+// Step 2: codes, scale bytes and the row global (no barrier; call only for real rows).
+template <int BPT>
+__device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], int NB, int t,
+                                                   int nthreads, float amax,
+                                                   uint8_t* __restrict__ q,
+                                                   uint8_t* __restrict__ sc,
+                                                   float* __restrict__ gs_out) {
+#pragma clang fp contract(off)
+  const float gs = amax > 0.0f ? amax / 2688.0f : 1.0f;
+  const float tg = 6.0f * gs;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int b = t + nthreads * k;
+    if (b >= NB) continue;
+    float bmax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, __builtin_fabsf(v[k][e]));
+    const float sf = bmax / tg;
+    const uint32_t sb = e4m3_encode_pos(sf);
+    const float d = e4m3_to_f32(sb) * gs;
+    uint32_t lo = 0, hi = 0;
+    if (d != 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo |= e2m1_encode(v[k][e] / d) << (4 * e);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hi |= e2m1_encode(v[k][8 + e] / d) << (4 * e);
+    }
+    u32x2 pk = {lo, hi};
+    *(u32x2*)(q + 8 * (size_t)b) = pk;
+    sc[b] = (uint8_t)sb;
+  }
+  if (t == 0) *gs_out = gs;
+}
+
+// Threads per row for NB scale blocks: a multiple of 64, at most 256.
+static inline int row_threads(int NB) {
+  const int t = ((NB + 63) / 64) * 64;
+  return t < 256 ? t : 256;
+}
+
 }  // namespace moe
 
 // ------------------------------------------------------------------ internal launchers
@@ -121,12 +204,24 @@ hipError_t launch_gather(const uint16_t* x, int H, const int32_t* row_src, int R
                          hipStream_t s);
 hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, int R, int K, uint8_t* q,
                            uint8_t* sc, float* row_gs, hipStream_t s);
+// row_gs of grouped row i is row_gs[gs_map[i]] (gs_map == nullptr: row_gs[i]).
 hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* expert_offsets, int E,
                          const float* g_gate, const float* g_up, const float* row_gs,
-                         uint16_t* h, uint8_t* q, uint8_t* sc, float* h_gs, hipStream_t s);
-hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* expert_offsets,
-                               int E, int R, const uint8_t* w, int N, int K, float* out,
-                               int flags, int gemv_max_rows, hipStream_t s);
+                         const int32_t* gs_map, uint16_t* h, uint8_t* q, uint8_t* sc,
+                         float* h_gs, hipStream_t s);
+// Activation row of grouped row i is amap[i] (amap == nullptr: row i) of a_rows rows.
+hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
+                               int a_rows, const int32_t* expert_offsets, int E, const uint8_t* w,
+                               int N, int K, float* out, int flags, int gemv_max_rows,
+                               hipStream_t s);
+// Grouping and NVFP4 quantization of the S source rows of x in one launch (independent
+// work: block 0 groups, the other blocks quantize four rows each).
+hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
+                                 const float* a_w, int R, int E, int S, int T,
+                                 int32_t* expert_offsets, int32_t* row_src, int32_t* row_dst,
+                                 float* row_w, int32_t* tok_off, int32_t* tok_rows,
+                                 int32_t* err_word, const uint16_t* x, int H, uint8_t* xq,
+                                 uint8_t* xs, float* xgs, hipStream_t s);
 hipError_t launch_scatter(const float* y, int R, int H, const int32_t* expert_offsets, int E,
                           const float* row_w, const float* g_down, const float* row_gs,
                           const int32_t* tok_off, const int32_t* tok_rows, int T, uint16_t* out,

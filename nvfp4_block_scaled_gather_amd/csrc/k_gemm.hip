@@ -28,19 +28,22 @@
 #include <mutex>
 
 #ifndef MOE_GEMM_NS
-#define MOE_GEMM_NS 4  // 16-row tiles per wave, MFMA kernel
+#define MOE_GEMM_NS 2  // 16-row tiles per wave, MFMA kernel
 #endif
 #ifndef MOE_GEMM_D
-#define MOE_GEMM_D 2   // chunks in flight per wave, MFMA kernel
+#define MOE_GEMM_D 4   // chunks in flight per wave, MFMA kernel
 #endif
 #ifndef MOE_GEMM_CT
-#define MOE_GEMM_CT 2  // 16-row activation column tiles per MFMA pass
+#define MOE_GEMM_CT 1  // 16-row activation column tiles per MFMA pass
 #endif
 #ifndef MOE_GEMV_NS
 #define MOE_GEMV_NS 2  // 16-row tiles per wave, GEMV kernel
 #endif
 #ifndef MOE_GEMV_D
 #define MOE_GEMV_D 2
+#endif
+#ifndef MOE_GEMM_WGS_PER_CU
+#define MOE_GEMM_WGS_PER_CU 0  // 0: one work item per workgroup; n > 0: persistent, n per CU
 #endif
 
 namespace moe {
@@ -49,8 +52,10 @@ constexpr int kGemmWaves = 4;
 constexpr int kGemvRows = 4;
 
 struct GemmArgs {
-  const uint8_t* aq;
-  const uint8_t* as;
+  const uint8_t* aq;     // activation rows [A, K/2] (A = a_rows)
+  const uint8_t* as;     // their scales [A, K/16]
+  const int32_t* amap;   // grouped row i reads activation row amap[i]; nullptr: row i
+  int a_rows;
   const int32_t* off;
   int E;
   const uint8_t* w;
@@ -59,22 +64,33 @@ struct GemmArgs {
   int gmin, gmax;  // this kernel's groups: gmin <= G <= gmax
 };
 
+// Activation row of grouped row i (i < rows of the pass); -1 when the lane has no row.
+__device__ __forceinline__ int act_row(const GemmArgs& p, int i, bool valid) {
+  if (!valid) return -1;
+  return p.amap ? p.amap[i] : i;
+}
+
 // Ids of the experts whose group size is in [gmin, gmax], ascending, into LDS (wave 0).
 __device__ __forceinline__ int build_active_list(const GemmArgs& p, uint16_t* s_act, int* s_nact) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     int n = 0;
-    for (int base = 0; base < p.E; base += 64) {
-      const int e = base + lane;
-      bool a = false;
-      if (e < p.E) {
-        const int g = p.off[e + 1] - p.off[e];
-        a = g >= p.gmin && g <= p.gmax;
+    for (int base = 0; base < p.E; base += 256) {
+      int g[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // four independent loads in flight
+        const int e = base + 64 * u + lane;
+        g[u] = e < p.E ? p.off[e + 1] - p.off[e] : 0;
       }
-      const uint64_t m = __ballot(a);
-      if (a) s_act[n + __popcll(m & below)] = (uint16_t)e;
-      n += __popcll(m);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = base + 64 * u + lane;
+        const bool a = e < p.E && g[u] >= p.gmin && g[u] <= p.gmax;
+        const uint64_t m = __ballot(a);
+        if (a) s_act[n + __popcll(m & below)] = (uint16_t)e;
+        n += __popcll(m);
+      }
     }
     if (lane == 0) *s_nact = n;
   }
@@ -82,24 +98,37 @@ __device__ __forceinline__ int build_active_list(const GemmArgs& p, uint16_t* s_
   return *s_nact;
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets beyond the range return 0,
+// which zero-fills the activation rows a pass does not own without any branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+#ifndef MOE_W_CPOL
+#define MOE_W_CPOL 2  // cache policy of the weight-stream loads: non-temporal (read once)
+#endif
+
 // ------------------------------------------------------------------------- MFMA path
+// One pass over K for NS weight tiles (wt: first tile, uniform) and CT activation column
+// tiles (rows arow0 .. arow0 + nrows - 1).  NC % D == 0.
 template <int NS, int D, int CT>
 __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0) {
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, r = lane & 15;
   const int K = p.K, NC = K / 128;
-  const size_t tstride = (size_t)NC * kChunkBytes;
-
-  const uint8_t* aqp[CT];
-  const uint8_t* asp[CT];
-  bool av[CT];
+  const int tstride = NC * kChunkBytes;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, nsv * tstride);
+  const int abytes = p.a_rows * (K / 2), sbytes = p.a_rows * (K / 16);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, abytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, sbytes);
+  const int vw = 16 * lane, vws = 1024 + 2 * lane;
+  int va[CT], vs[CT];  // lanes without a row point past the end: their loads return 0
 #pragma unroll
   for (int a = 0; a < CT; ++a) {
-    av[a] = 16 * a + r < nrows;
-    const int row = arow0 + (av[a] ? 16 * a + r : 0);
-    aqp[a] = p.aq + (size_t)row * (K / 2) + 16 * kq;
-    asp[a] = p.as + (size_t)row * (K / 16) + 2 * kq;
+    const int row = act_row(p, arow0 + 16 * a + r, 16 * a + r < nrows);
+    va[a] = row >= 0 ? row * (K / 2) + 16 * kq : abytes;
+    vs[a] = row >= 0 ? row * (K / 16) + 2 * kq : sbytes;
   }
 
   u32x4 wn[D][NS];
@@ -113,37 +142,25 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     for (int a = 0; a < CT; ++a) acc[s][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto load = [&](int c, int slot) {
-    const size_t off = (size_t)c * kChunkBytes;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s < nsv) {
-        const uint8_t* t = wt + s * tstride + off;
-        wn[slot][s] = *(const u32x4*)(t + 16 * lane);
-        ws[slot][s] = *(const uint16_t*)(t + 1024 + 2 * lane);
-      }
+      const int so = s * tstride + c * kChunkBytes;
+      wn[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(wr, vw, so, MOE_W_CPOL);
+      ws[slot][s] = __builtin_amdgcn_raw_buffer_load_b16(wr, vws, so, MOE_W_CPOL);
     }
 #pragma unroll
     for (int a = 0; a < CT; ++a) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      uint32_t zs = 0u;
-      if (av[a]) {
-        z = *(const u32x4*)(aqp[a] + 64 * c);
-        zs = *(const uint16_t*)(asp[a] + 8 * c);
-      }
-      an[slot][a] = z;
-      asc[slot][a] = zs;
+      an[slot][a] = __builtin_amdgcn_raw_buffer_load_b128(ar, va[a], 64 * c, 0);
+      asc[slot][a] = __builtin_amdgcn_raw_buffer_load_b16(sr, vs[a], 8 * c, 0);
     }
   };
 
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < NC) load(d, d);
+  for (int d = 0; d < D; ++d) load(d, d);
 
   for (int c0 = 0; c0 < NC; c0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int c = c0 + d;
-      if (c >= NC) break;
       f16x8 bop[CT][4];
 #pragma unroll
       for (int a = 0; a < CT; ++a) {
@@ -156,7 +173,6 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
       }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        if (s >= nsv) continue;
         const uint32_t w0 = e4m3_to_f16x2_scaled(ws[d][s] & 0xFFu);
         const uint32_t w1 = e4m3_to_f16x2_scaled(ws[d][s] >> 8);
 #pragma unroll
@@ -167,21 +183,37 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
             acc[s][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[a][j], acc[s][a], 0, 0, 0);
         }
       }
-      if (c + D < NC) load(c + D, d);
+      if (c0 + d + D < NC) load(c0 + d + D, d);
     }
   }
 
   // lane l holds out rows (16a + r) x weight rows 4 kq .. 4 kq + 3 of each tile
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (s >= nsv) continue;
+    if (s >= nsv) break;
 #pragma unroll
     for (int a = 0; a < CT; ++a) {
-      if (!av[a]) continue;
-      const int row = arow0 + 16 * a + r;
-      *(f32x4*)(p.out + (size_t)row * p.N + col0 + 16 * s + 4 * kq) = acc[s][a];
+      if (16 * a + r < nrows) {
+        const int row = arow0 + 16 * a + r;
+        *(f32x4*)(p.out + (size_t)row * p.N + col0 + 16 * s + 4 * kq) = acc[s][a];
+      }
     }
   }
+}
+
+// Item loop shared by both kernels: item -> (expert, first tile of this wave).
+struct ItemLoop {
+  int nact, items_per_e, total, tiles, per_item;
+};
+
+__device__ __forceinline__ ItemLoop item_loop(const GemmArgs& p, int nact, int NS) {
+  ItemLoop L;
+  L.nact = nact;
+  L.tiles = p.N / 16;
+  L.per_item = kGemmWaves * NS;
+  L.items_per_e = (L.tiles + L.per_item - 1) / L.per_item;
+  L.total = nact * L.items_per_e;
+  return L;
 }
 
 template <int NS, int D, int CT>
@@ -189,19 +221,17 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
   extern __shared__ uint16_t s_act[];
   __shared__ int s_nact;
   const int nact = build_active_list(p, s_act, &s_nact);
-  const int wave = threadIdx.x >> 6;
-  const int tiles = p.N / 16;
-  const int per_item = kGemmWaves * NS;
-  const int items_per_e = (tiles + per_item - 1) / per_item;
-  const int total = nact * items_per_e;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const ItemLoop L = item_loop(p, nact, NS);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    const int e = s_act[it / items_per_e];
-    const int t0 = (it % items_per_e) * per_item + wave * NS;
-    const int nsv = min(NS, tiles - t0);
+  for (int it = blockIdx.x; it < L.total; it += gridDim.x) {
+    const int e = __builtin_amdgcn_readfirstlane(s_act[it / L.items_per_e]);
+    const int t0 = (it % L.items_per_e) * L.per_item + wave * NS;
+    const int nsv = min(NS, L.tiles - t0);
     if (nsv <= 0) continue;
-    const int r0 = p.off[e], G = p.off[e + 1] - r0;
+    const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
+    const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
     const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)t0 * tile_bytes;
     for (int b = 0; b < G; b += 16 * CT)
       mfma_pass<NS, D, CT>(p, wt, nsv, r0 + b, min(16 * CT, G - b), 16 * t0);
@@ -216,15 +246,18 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4;
   const int K = p.K, NC = K / 128;
-  const size_t tstride = (size_t)NC * kChunkBytes;
-
-  const uint8_t* aqp[NR];
-  const uint8_t* asp[NR];
+  const int tstride = NC * kChunkBytes;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, nsv * tstride);
+  const int abytes = p.a_rows * (K / 2), sbytes = p.a_rows * (K / 16);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, abytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, sbytes);
+  const int vw = 16 * lane, vws = 1024 + 2 * lane;
+  int va[NR], vs[NR];
 #pragma unroll
   for (int a = 0; a < NR; ++a) {
-    const int row = arow0 + (a < nrows ? a : 0);
-    aqp[a] = p.aq + (size_t)row * (K / 2) + 16 * kq;
-    asp[a] = p.as + (size_t)row * (K / 16) + 2 * kq;
+    const int row = act_row(p, arow0 + a, a < nrows);
+    va[a] = row >= 0 ? row * (K / 2) + 16 * kq : abytes;
+    vs[a] = row >= 0 ? row * (K / 16) + 2 * kq : sbytes;
   }
 
   u32x4 wn[D][NS];
@@ -238,70 +271,52 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
     for (int a = 0; a < NR; ++a) acc[s][a] = 0.f;
 
   auto load = [&](int c, int slot) {
-    const size_t off = (size_t)c * kChunkBytes;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s < nsv) {
-        const uint8_t* t = wt + s * tstride + off;
-        wn[slot][s] = *(const u32x4*)(t + 16 * lane);
-        ws[slot][s] = *(const uint16_t*)(t + 1024 + 2 * lane);
-      }
+      const int so = s * tstride + c * kChunkBytes;
+      wn[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(wr, vw, so, MOE_W_CPOL);
+      ws[slot][s] = __builtin_amdgcn_raw_buffer_load_b16(wr, vws, so, MOE_W_CPOL);
     }
 #pragma unroll
     for (int a = 0; a < NR; ++a) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      uint32_t zs = 0u;
-      if (a < nrows) {
-        z = *(const u32x4*)(aqp[a] + 64 * c);
-        zs = *(const uint16_t*)(asp[a] + 8 * c);
-      }
-      an[slot][a] = z;
-      asc[slot][a] = zs;
+      an[slot][a] = __builtin_amdgcn_raw_buffer_load_b128(ar, va[a], 64 * c, 0);
+      asc[slot][a] = __builtin_amdgcn_raw_buffer_load_b16(sr, vs[a], 8 * c, 0);
     }
   };
 
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < NC) load(d, d);
+  for (int d = 0; d < D; ++d) load(d, d);
 
   for (int c0 = 0; c0 < NC; c0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int c = c0 + d;
-      if (c >= NC) break;
-      // activation segments, exact f16 (codes times their block scales)
-      f16x2 xa[NR][16];
-#pragma unroll
-      for (int a = 0; a < NR; ++a) {
-        const uint32_t s0 = e4m3_to_f16x2_scaled(asc[d][a] & 0xFFu);
-        const uint32_t s1 = e4m3_to_f16x2_scaled(asc[d][a] >> 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x8 v = dequant8(an[d][a][j], j < 2 ? s0 : s1);
-#pragma unroll
-          for (int m = 0; m < 4; ++m) xa[a][4 * j + m] = f16x2{v[2 * m], v[2 * m + 1]};
-        }
-      }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        if (s >= nsv) continue;
         const float sw0 = e4m3_to_f32(ws[d][s] & 0xFFu), sw1 = e4m3_to_f32(ws[d][s] >> 8);
         f16x2 wv[16];
 #pragma unroll
         for (int j = 0; j < 4; ++j) e2m1x8_to_f16(wn[d][s][j], &wv[4 * j]);
 #pragma unroll
         for (int a = 0; a < NR; ++a) {
-          if (a >= nrows) continue;
+          if (a >= nrows) break;  // uniform
+          const uint32_t s0 = e4m3_to_f16x2_scaled(asc[d][a] & 0xFFu);
+          const uint32_t s1 = e4m3_to_f16x2_scaled(asc[d][a] >> 8);
           float b0 = 0.f, b1 = 0.f;
 #pragma unroll
-          for (int m = 0; m < 8; ++m) b0 = __builtin_amdgcn_fdot2(wv[m], xa[a][m], b0, false);
+          for (int j = 0; j < 4; ++j) {
+            const f16x8 v = dequant8(an[d][a][j], j < 2 ? s0 : s1);
 #pragma unroll
-          for (int m = 8; m < 16; ++m) b1 = __builtin_amdgcn_fdot2(wv[m], xa[a][m], b1, false);
+            for (int m = 0; m < 4; ++m) {
+              const f16x2 x2 = f16x2{v[2 * m], v[2 * m + 1]};
+              if (j < 2) b0 = __builtin_amdgcn_fdot2(wv[4 * j + m], x2, b0, false);
+              else b1 = __builtin_amdgcn_fdot2(wv[4 * j + m], x2, b1, false);
+            }
+          }
           acc[s][a] = fmaf(sw0, b0, acc[s][a]);
           acc[s][a] = fmaf(sw1, b1, acc[s][a]);
         }
       }
-      if (c + D < NC) load(c + D, d);
+      if (c0 + d + D < NC) load(c0 + d + D, d);
     }
   }
 
@@ -323,19 +338,17 @@ __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
   extern __shared__ uint16_t s_act[];
   __shared__ int s_nact;
   const int nact = build_active_list(p, s_act, &s_nact);
-  const int wave = threadIdx.x >> 6;
-  const int tiles = p.N / 16;
-  const int per_item = kGemmWaves * NS;
-  const int items_per_e = (tiles + per_item - 1) / per_item;
-  const int total = nact * items_per_e;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const ItemLoop L = item_loop(p, nact, NS);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    const int e = s_act[it / items_per_e];
-    const int t0 = (it % items_per_e) * per_item + wave * NS;
-    const int nsv = min(NS, tiles - t0);
+  for (int it = blockIdx.x; it < L.total; it += gridDim.x) {
+    const int e = __builtin_amdgcn_readfirstlane(s_act[it / L.items_per_e]);
+    const int t0 = (it % L.items_per_e) * L.per_item + wave * NS;
+    const int nsv = min(NS, L.tiles - t0);
     if (nsv <= 0) continue;
-    const int r0 = p.off[e], G = p.off[e + 1] - r0;
+    const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
+    const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
     const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)t0 * tile_bytes;
     for (int b = 0; b < G; b += kGemvRows)
       gemv_pass<NS, D>(p, wt, nsv, r0 + b, min(kGemvRows, G - b), 16 * t0);
@@ -343,44 +356,60 @@ __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------------- launch
-struct LaunchLimits {
-  int occ = 0;  // workgroups per CU
-  int cus = 0;
-};
-
-template <typename Kern>
-static hipError_t limits_for(Kern kern, LaunchLimits* cache, std::mutex& mu, LaunchLimits* out) {
+static hipError_t cu_count(int* cus) {
+  static std::mutex mu;
+  static int cache[64] = {0};
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> g(mu);
-  if (!cache[dev].occ) {
-    int o = 0, c = 0;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, 256, 16384);
-    if (err != hipSuccess) return err;
+  if (!cache[dev]) {
+    int c = 0;
     err = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    cache[dev].occ = o > 0 ? o : 1;
-    cache[dev].cus = c > 0 ? c : 1;
+    cache[dev] = c > 0 ? c : 1;
   }
-  *out = cache[dev];
+  *cus = cache[dev];
   return hipSuccess;
 }
 
-static int persistent_grid(const LaunchLimits& l, int per_item, const GemmArgs& a) {
+// Workgroups to launch: every possible item (inactive ones exit after the prologue), or a
+// persistent grid of MOE_GEMM_WGS_PER_CU workgroups per CU.
+static int gemm_grid(int per_item, const GemmArgs& a, int cus) {
   const long items_per_e = (a.N / 16 + per_item - 1) / per_item;
   const long max_items = items_per_e * a.E;
-  const long slots = (long)l.occ * l.cus;
+  if (MOE_GEMM_WGS_PER_CU <= 0) return (int)max_items;
+  const long slots = (long)MOE_GEMM_WGS_PER_CU * cus;
   return (int)(max_items < slots ? max_items : slots);
 }
 
-hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* off, int E,
-                               int R, const uint8_t* w, int N, int K, float* out, int flags,
-                               int gemv_max_rows, hipStream_t s) {
-  (void)R;
-  static std::mutex mu;
-  static LaunchLimits mfma_cache[64], gemv_cache[64];
+// Ring depth: the configured depth, reduced until it divides the chunk count K / 128.
+static int ring_depth(int K, int dmax) {
+  const int nc = K / 128;
+  int d = dmax;
+  while (d > 1 && nc % d) d >>= 1;
+  return d;
+}
+
+template <int D>
+static void launch_mfma_d(const GemmArgs& a, int cus, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_mfma<MOE_GEMM_NS, D, MOE_GEMM_CT>),
+                     dim3(gemm_grid(kGemmWaves * MOE_GEMM_NS, a, cus)), dim3(256), lds, s, a);
+}
+
+template <int D>
+static void launch_gemv_d(const GemmArgs& a, int cus, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_gemv<MOE_GEMV_NS, D>),
+                     dim3(gemm_grid(kGemmWaves * MOE_GEMV_NS, a, cus)), dim3(256), lds, s, a);
+}
+
+hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
+                               int a_rows, const int32_t* off, int E, const uint8_t* w, int N, int K,
+                               float* out, int flags, int gemv_max_rows, hipStream_t s) {
+  int cus = 0;
+  hipError_t err = cu_count(&cus);
+  if (err != hipSuccess) return err;
   const size_t lds = sizeof(uint16_t) * (size_t)E;
   const int big = 0x7FFFFFFF;
   // which groups each kernel owns
@@ -393,22 +422,22 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
     mfma_lo = gemv_max_rows + 1;
   }
   if (gemv_hi >= gemv_lo) {
-    GemmArgs a{aq, as, off, E, w, N, K, out, gemv_lo, gemv_hi};
-    auto kern = k_gemm_gemv<MOE_GEMV_NS, MOE_GEMV_D>;
-    LaunchLimits l;
-    hipError_t err = limits_for(kern, gemv_cache, mu, &l);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(persistent_grid(l, kGemmWaves * MOE_GEMV_NS, a)), dim3(256), lds, s, a);
+    const GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, gemv_lo, gemv_hi};
+    switch (ring_depth(K, MOE_GEMV_D)) {
+      case 1: launch_gemv_d<1>(a, cus, lds, s); break;
+      case 2: launch_gemv_d<2>(a, cus, lds, s); break;
+      default: launch_gemv_d<(MOE_GEMV_D >= 4 ? 4 : MOE_GEMV_D)>(a, cus, lds, s); break;
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (mfma_lo < big) {
-    GemmArgs a{aq, as, off, E, w, N, K, out, mfma_lo < 1 ? 1 : mfma_lo, big};
-    auto kern = k_gemm_mfma<MOE_GEMM_NS, MOE_GEMM_D, MOE_GEMM_CT>;
-    LaunchLimits l;
-    hipError_t err = limits_for(kern, mfma_cache, mu, &l);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3(persistent_grid(l, kGemmWaves * MOE_GEMM_NS, a)), dim3(256), lds, s, a);
+    const GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, mfma_lo < 1 ? 1 : mfma_lo, big};
+    switch (ring_depth(K, MOE_GEMM_D)) {
+      case 1: launch_mfma_d<1>(a, cus, lds, s); break;
+      case 2: launch_mfma_d<2>(a, cus, lds, s); break;
+      default: launch_mfma_d<(MOE_GEMM_D >= 4 ? 4 : MOE_GEMM_D)>(a, cus, lds, s); break;
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -1,19 +1,20 @@
-// Row grouping (stable counting sort by expert id, then by output row) and row gather.
+// Row grouping (stable sort by expert id, then by output row), row gather, and the fused
+// grouping + source-row quantization launch of the layer.
 //
 // One workgroup does the whole grouping: R is at most a few thousand expert-rows per
-// layer step, so the work is latency-bound and one CU with LDS histograms is enough.
-//   1. every thread validates its assignments, counts them per expert (invalid ones in
-//      an extra bucket E) and per output row, ORs error bits;
-//   2. exclusive scans of both histograms (expert_offsets, tok_off);
-//   3. wave 0 places assignments in (expert, j) order, 64 at a time: within a batch the
-//      lanes holding the same key find each other with one ballot per key bit, so a
-//      lane's rank is the popcount of equal-key lanes below it — no atomics, stable;
-//   4. wave 0 places grouped rows into the token lists the same way, in ascending i.
+// layer step, so the work is latency-bound and one CU with LDS is enough:
+//   1. every thread validates its assignments, counts them per expert (invalid ones in an
+//      extra bucket E) and per output row, and ORs error bits;
+//   2. exclusive scans of both histograms give expert_offsets and tok_off;
+//   3. assignments are placed in (expert, j) order and 4. grouped rows into the token
+//      lists in ascending i, both by stable_place: all 16 waves when per-wave histograms
+//      of the keys fit in LDS (E and T up to about 900), else one wave.
 #include "common.h"
 
 namespace moe {
 
 constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / 64;
 
 // Lanes of the wave whose `key` equals this lane's key (keys < 2^bits).
 __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits, bool active) {
@@ -43,12 +44,12 @@ __device__ int block_exclusive_scan(int* cnt, int n, int* s_part) {
   if (lane == 63) s_part[wave] = v;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kGroupThreads / 64 ? s_part[lane] : 0;
+    int w = lane < kGroupWaves ? s_part[lane] : 0;
     for (int d = 1; d < 64; d <<= 1) {
       const int o = __shfl_up(w, d, 64);
       if (lane >= d) w += o;
     }
-    if (lane < kGroupThreads / 64) s_part[lane] = w;  // inclusive wave prefix
+    if (lane < kGroupWaves) s_part[lane] = w;  // inclusive wave prefix
   }
   __syncthreads();
   int run = v - local + (wave ? s_part[wave - 1] : 0);  // exclusive prefix of this thread
@@ -57,28 +58,85 @@ __device__ int block_exclusive_scan(int* cnt, int n, int* s_part) {
     cnt[k] = run;
     run += c;
   }
-  const int total = s_part[kGroupThreads / 64 - 1];
+  const int total = s_part[kGroupWaves - 1];
   __syncthreads();
   return total;
 }
 
-__global__ __launch_bounds__(kGroupThreads) void k_group(
-    const int32_t* __restrict__ a_expert, const int32_t* __restrict__ a_src,
-    const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R, int E, int S, int T,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
-    float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
-    int32_t* __restrict__ err_word) {
-  extern __shared__ int lds[];
-  int* cnt_e = lds;              // E + 1 (bucket E = dropped assignments)
-  int* cnt_t = lds + (E + 1);    // T + 1
-  __shared__ int s_part[kGroupThreads / 64];
+// Stable counting sort of n items by key (< nkeys), into positions starting at
+// bucket_start[key] (an exclusive prefix of the key counts; used as scratch).
+// With nw = 16 waves, wave w owns the contiguous segment [w*seg, (w+1)*seg): per-wave key
+// histograms (hist, 16 x nkeys ints of LDS) turn the bucket starts into per-(wave, key)
+// cursors.  With nw = 1, wave 0 walks all items and bucket_start itself is the cursor.
+// Inside a wave items go 64 at a time; lanes holding equal keys find each other with one
+// ballot per key bit, so a lane's rank is the number of equal-key lanes below it.
+// Resulting order: (key, item index) — stable and deterministic.
+template <typename KeyFn, typename PlaceFn>
+__device__ void stable_place(int n, int nkeys, int* bucket_start, int* hist, int nw,
+                             KeyFn key_of, PlaceFn place) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = (n + nw - 1) / nw;
+  const int j0 = wave < nw ? wave * seg : n, j1 = min(n, j0 + seg);
+  int* h = bucket_start;
+  if (nw > 1) {
+    h = hist + wave * nkeys;
+    for (int k = tid; k < nw * nkeys; k += kGroupThreads) hist[k] = 0;
+    __syncthreads();
+    for (int j = j0 + lane; j < j1; j += 64) atomicAdd(&h[key_of(j)], 1);
+    __syncthreads();
+    for (int b = tid; b < nkeys; b += kGroupThreads) {
+      int run = bucket_start[b];
+      for (int w = 0; w < nw; ++w) {
+        const int c = hist[w * nkeys + b];
+        hist[w * nkeys + b] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+  }
+  int bits = 1;
+  while ((1 << bits) < nkeys) ++bits;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int base = j0; base < j1; base += 64) {
+    const int j = base + lane;
+    const bool act = j < j1;
+    const int key = act ? key_of(j) : 0;
+    const uint64_t same = match_key((uint32_t)key, bits, act);
+    const int rank = __popcll(same & below);
+    const int pos = act ? h[key] + rank : 0;
+    if (act) {
+      place(j, pos);
+      if (rank == __popcll(same) - 1) h[key] = pos + 1;  // last lane of its key
+    }
+  }
+  __syncthreads();
+}
+
+// LDS ints the grouping needs: the two histograms, plus the per-wave ones when parallel.
+__host__ __device__ inline size_t group_lds_ints(int E, int T, bool parallel) {
+  const size_t base = (size_t)(E + 1) + (size_t)(T + 1);
+  return parallel ? base + (size_t)kGroupWaves * (size_t)((E > T ? E : T) + 1) : base;
+}
+
+// The whole grouping, by one workgroup of kGroupThreads threads.
+__device__ void group_body(const int32_t* __restrict__ a_expert, const int32_t* __restrict__ a_src,
+                           const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R,
+                           int E, int S, int T, int32_t* __restrict__ expert_offsets,
+                           int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
+                           float* __restrict__ row_w, int32_t* __restrict__ tok_off,
+                           int32_t* __restrict__ tok_rows, int32_t* __restrict__ err_word,
+                           bool parallel, int* lds) {
+  int* cnt_e = lds;                     // E + 1 (bucket E = dropped assignments)
+  int* cnt_t = lds + (E + 1);           // T + 1
+  int* hist = lds + (E + 1) + (T + 1);  // kGroupWaves x (max(E, T) + 1) when parallel
+  __shared__ int s_part[kGroupWaves];
   __shared__ int s_err;
   const int tid = threadIdx.x;
+  const int nw = parallel ? kGroupWaves : 1;
   for (int k = tid; k < E + 1; k += kGroupThreads) cnt_e[k] = 0;
   for (int k = tid; k < T + 1; k += kGroupThreads) cnt_t[k] = 0;
   if (tid == 0) s_err = 0;
   __syncthreads();
-
   // 1. validate and count
   int err = 0;
   for (int j = tid; j < R; j += kGroupThreads) {
@@ -93,80 +151,118 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(
   }
   if (err) atomicOr(&s_err, err);
   __syncthreads();
-
-  // 2. scans
+  // 2. bucket starts
   block_exclusive_scan(cnt_e, E + 1, s_part);
   block_exclusive_scan(cnt_t, T + 1, s_part);
   for (int k = tid; k < E + 1; k += kGroupThreads) expert_offsets[k] = cnt_e[k];
   for (int k = tid; k < T + 1; k += kGroupThreads) tok_off[k] = cnt_t[k];
   if (tid == 0) *err_word = s_err;
-  __syncthreads();  // offsets read back below from LDS only
-
-  int ebits = 1;
-  while ((1 << ebits) < E + 1) ++ebits;
-  int tbits = 1;
-  while ((1 << tbits) < T + 1) ++tbits;
-
-  // 3. stable placement by expert (wave 0; cnt_e now holds running cursors)
-  if (tid < 64) {
-    const int lane = tid;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < R; base += 64) {
-      const int j = base + lane;
-      const bool act = j < R;
-      int key = E, s = -1, d = -1;
-      float w = 0.f;
-      if (act) {
-        const int e = a_expert[j];
-        s = a_src[j];
-        d = a_dst[j];
-        const bool ok = e >= 0 && e < E && s >= 0 && s < S && d >= 0 && d < T;
-        key = ok ? e : E;
-        if (ok) w = a_w[j];
-        else { s = -1; d = -1; }
-      }
-      const uint64_t same = match_key((uint32_t)key, ebits, act);
-      const int rank = __popcll(same & below);
-      const int cur = act ? cnt_e[key] : 0;
-      const int pos = cur + rank;
-      if (act) {
-        row_src[pos] = s;
-        row_dst[pos] = d;
-        row_w[pos] = w;
-        if (rank == __popcll(same) - 1) cnt_e[key] = pos + 1;  // last lane of its key
-      }
-    }
-  }
+  const int Rv = cnt_e[E];
   __syncthreads();
+  // 3. grouped rows in (expert, assignment) order; dropped assignments last
+  auto key_e = [&](int j) -> int {
+    const int e = a_expert[j], s = a_src[j], d = a_dst[j];
+    const bool ok = e >= 0 && e < E && s >= 0 && s < S && d >= 0 && d < T;
+    return ok ? e : E;
+  };
+  stable_place(R, E + 1, cnt_e, hist, nw, key_e, [&](int j, int pos) {
+    const bool ok = pos < Rv;
+    row_src[pos] = ok ? a_src[j] : -1;
+    row_dst[pos] = ok ? a_dst[j] : -1;
+    row_w[pos] = ok ? a_w[j] : 0.f;
+  });
+  // 4. token lists, ascending grouped row (row_dst is visible after stable_place's barrier)
+  stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return row_dst[i]; },
+               [&](int i, int pos) { tok_rows[pos] = i; });
+}
 
-  // 4. token lists in ascending grouped row (wave 0; cnt_t holds running cursors)
-  if (tid < 64) {
-    const int lane = tid;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int Rv = expert_offsets[E];
-    for (int base = 0; base < Rv; base += 64) {
-      const int i = base + lane;
-      const bool act = i < Rv;
-      const int d = act ? row_dst[i] : 0;
-      const uint64_t same = match_key((uint32_t)d, tbits, act);
-      const int rank = __popcll(same & below);
-      const int cur = act ? cnt_t[d] : 0;
-      if (act) {
-        tok_rows[cur + rank] = i;
-        if (rank == __popcll(same) - 1) cnt_t[d] = cur + rank + 1;
-      }
-    }
+__global__ __launch_bounds__(kGroupThreads) void k_group(
+    const int32_t* __restrict__ a_expert, const int32_t* __restrict__ a_src,
+    const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R, int E, int S, int T,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
+    float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
+    int32_t* __restrict__ err_word, bool parallel) {
+  extern __shared__ int lds[];
+  group_body(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w,
+             tok_off, tok_rows, err_word, parallel, lds);
+}
+
+// Grouping (block 0) and NVFP4 quantization of the S source rows of x (the other blocks,
+// 1024 / nthreads rows each) in one launch: the two are independent, since a row's codes
+// depend only on the row.
+template <int BPT>
+__global__ __launch_bounds__(kGroupThreads) void k_group_quantize(
+    const int32_t* __restrict__ a_expert, const int32_t* __restrict__ a_src,
+    const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R, int E, int S, int T,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
+    float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
+    int32_t* __restrict__ err_word, bool parallel, const uint16_t* __restrict__ x, int H,
+    int nthreads, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, float* __restrict__ xgs) {
+  extern __shared__ int lds[];
+  __shared__ float s_red[kGroupWaves];
+  if (blockIdx.x == 0) {
+    group_body(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w,
+               tok_off, tok_rows, err_word, parallel, lds);
+    return;
   }
+  const int rows_per_block = kGroupThreads / nthreads;
+  const int slot = threadIdx.x / nthreads, t = threadIdx.x % nthreads;
+  const int row = (blockIdx.x - 1) * rows_per_block + slot;
+  const bool active = row < S;
+  const int NB = H / 16;
+  float v[BPT][16];
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int b = t + nthreads * k;
+    u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+    if (active && b < NB) {
+      const u32x4* p = (const u32x4*)(x + (size_t)row * H + 16 * b);
+      w0 = p[0];
+      w1 = p[1];
+    }
+    bf16x16_to_f32(w0, w1, v[k]);
+  }
+  // every thread takes part in the row-max barrier; only the slots of real rows store
+  const float amax = row_amax_threads<BPT>(v, t, nthreads, s_red + slot * (nthreads / 64));
+  if (active)
+    quantize_row_store<BPT>(v, NB, t, nthreads, amax, xq + (size_t)row * (H / 2),
+                            xs + (size_t)row * NB, xgs + row);
+}
+
+static bool group_parallel(int E, int T) {
+  return group_lds_ints(E, T, true) * sizeof(int) <= 65536;
 }
 
 hipError_t launch_group(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
                         const float* a_w, int R, int E, int S, int T, int32_t* expert_offsets,
                         int32_t* row_src, int32_t* row_dst, float* row_w, int32_t* tok_off,
                         int32_t* tok_rows, int32_t* err_word, hipStream_t s) {
-  const size_t lds = sizeof(int) * (size_t)(E + 1 + T + 1);
-  hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), lds, s, a_expert, a_src, a_dst, a_w,
-                     R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off, tok_rows,
-                     err_word);
+  const bool par = group_parallel(E, T);
+  hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), group_lds_ints(E, T, par) * sizeof(int),
+                     s, a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
+                     row_w, tok_off, tok_rows, err_word, par);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
+                                 const float* a_w, int R, int E, int S, int T,
+                                 int32_t* expert_offsets, int32_t* row_src, int32_t* row_dst,
+                                 float* row_w, int32_t* tok_off, int32_t* tok_rows,
+                                 int32_t* err_word, const uint16_t* x, int H, uint8_t* xq,
+                                 uint8_t* xs, float* xgs, hipStream_t s) {
+  const bool par = group_parallel(E, T);
+  const int NB = H / 16, nt = row_threads(NB);
+  const int rows_per_block = kGroupThreads / nt;
+  const dim3 grid(1 + (S + rows_per_block - 1) / rows_per_block);
+  const size_t lds = group_lds_ints(E, T, par) * sizeof(int);
+  if (NB <= 256)
+    hipLaunchKernelGGL(k_group_quantize<1>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
+                       a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
+                       tok_rows, err_word, par, x, H, nt, xq, xs, xgs);
+  else
+    hipLaunchKernelGGL(k_group_quantize<2>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
+                       a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
+                       tok_rows, err_word, par, x, H, nt, xq, xs, xgs);
   return hipGetLastError();
 }
 

@@ -1,114 +1,56 @@
 // Row-wise kernels: NVFP4 quantization (optionally gathering its input rows), SwiGLU fused
-// with the re-quantization, and the weighted scatter-add.  One wavefront owns one row, so
-// every row reduction (amax, sums) stays inside a wave and its order is fixed.
+// with the re-quantization, and the weighted scatter-add.
+//
+// Quantize / SwiGLU: one workgroup per row, one thread per 16-element scale block (two for
+// rows longer than 4096), so the per-element work (a correctly rounded division and an
+// e2m1 decision each) is spread over up to 256 threads and a row costs one pass.
 #include "common.h"
 
 namespace moe {
 
-// Largest power-of-two blocks-per-lane a row kernel keeps in registers (16 values each).
-constexpr int kMaxBPL = 8;  // rows of up to 64 * 8 * 16 = 8192 elements
-
-__device__ __forceinline__ float wave_max(float v) {
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-  return v;
-}
-
-// Quantize one row held in registers: lane owns blocks b = lane + 64k (k < BPL, b < NB),
-// v[k][0..15] the block's values.  Follows nvfp4_quantize_rows' definition exactly
-// (float32, correctly rounded divisions, no contraction).
-template <int BPL>
-__device__ __forceinline__ void quantize_row_regs(const float (&v)[BPL][16], int NB, int lane,
-                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
-                                                  float* __restrict__ gs_out) {
-#pragma clang fp contract(off)
-  float amax = 0.0f;
-#pragma unroll
-  for (int k = 0; k < BPL; ++k)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, __builtin_fabsf(v[k][e]));
-  amax = wave_max(amax);
-  const float gs = amax > 0.0f ? amax / 2688.0f : 1.0f;
-  const float t = 6.0f * gs;
-#pragma unroll
-  for (int k = 0; k < BPL; ++k) {
-    const int b = lane + 64 * k;
-    if (b >= NB) continue;
-    float bmax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, __builtin_fabsf(v[k][e]));
-    const float sf = bmax / t;
-    const uint32_t sb = e4m3_encode_pos(sf);
-    const float d = e4m3_to_f32(sb) * gs;
-    uint32_t lo = 0, hi = 0;
-    if (d != 0.0f) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lo |= e2m1_encode(v[k][e] / d) << (4 * e);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hi |= e2m1_encode(v[k][8 + e] / d) << (4 * e);
-    }
-    u32x2 pk = {lo, hi};
-    *(u32x2*)(q + 8 * (size_t)b) = pk;
-    sc[b] = (uint8_t)sb;
-  }
-  if (lane == 0) *gs_out = gs;
-}
-
 // ------------------------------------------------------------------------- quantize
-// One wave per output row i; its input is row row_map[i] (row_map == nullptr: row i;
+// One workgroup per output row i; its input is row row_map[i] (row_map == nullptr: row i;
 // a negative entry: an all-zero row).
-template <int BPL>
+template <int BPT>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ in,
-                                                  const int32_t* __restrict__ row_map, int R, int K,
+                                                  const int32_t* __restrict__ row_map, int K,
                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
                                                   float* __restrict__ row_gs) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;
+  __shared__ float s_red[4];
+  const int row = blockIdx.x;
   const int src = row_map ? row_map[row] : row;
   const int NB = K / 16;
-  float v[BPL][16];
+  float v[BPT][16];
 #pragma unroll
-  for (int k = 0; k < BPL; ++k) {
-    const int b = lane + 64 * k;
+  for (int k = 0; k < BPT; ++k) {
+    const int b = threadIdx.x + blockDim.x * k;
     u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
     if (b < NB && src >= 0) {
       const u32x4* p = (const u32x4*)(in + (size_t)src * K + 16 * b);
       w0 = p[0];
       w1 = p[1];
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[k][2 * e] = __uint_as_float(w0[e] << 16);
-      v[k][2 * e + 1] = __uint_as_float(w0[e] & 0xFFFF0000u);
-      v[k][8 + 2 * e] = __uint_as_float(w1[e] << 16);
-      v[k][8 + 2 * e + 1] = __uint_as_float(w1[e] & 0xFFFF0000u);
-    }
+    bf16x16_to_f32(w0, w1, v[k]);
   }
-  quantize_row_regs<BPL>(v, NB, lane, q + (size_t)row * (K / 2), sc + (size_t)row * NB,
-                         row_gs + row);
-}
-
-static int bpl_for(int NB) {
-  const int need = (NB + 63) / 64;
-  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  const float amax = row_amax_threads<BPT>(v, threadIdx.x, blockDim.x, s_red);
+  quantize_row_store<BPT>(v, NB, threadIdx.x, blockDim.x, amax, q + (size_t)row * (K / 2),
+                          sc + (size_t)row * NB, row_gs + row);
 }
 
 hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, int R, int K, uint8_t* q,
                            uint8_t* sc, float* row_gs, hipStream_t s) {
   if (R == 0) return hipSuccess;
-  const dim3 grid((R + 3) / 4), block(256);
-  switch (bpl_for(K / 16)) {
-    case 1: hipLaunchKernelGGL(k_quantize<1>, grid, block, 0, s, in, row_map, R, K, q, sc, row_gs); break;
-    case 2: hipLaunchKernelGGL(k_quantize<2>, grid, block, 0, s, in, row_map, R, K, q, sc, row_gs); break;
-    case 4: hipLaunchKernelGGL(k_quantize<4>, grid, block, 0, s, in, row_map, R, K, q, sc, row_gs); break;
-    default: hipLaunchKernelGGL(k_quantize<8>, grid, block, 0, s, in, row_map, R, K, q, sc, row_gs); break;
-  }
+  const int NB = K / 16, nt = row_threads(NB);
+  if (NB <= 256)
+    hipLaunchKernelGGL(k_quantize<1>, dim3(R), dim3(nt), 0, s, in, row_map, K, q, sc, row_gs);
+  else
+    hipLaunchKernelGGL(k_quantize<2>, dim3(R), dim3(nt), 0, s, in, row_map, K, q, sc, row_gs);
   return hipGetLastError();
 }
 
-// Expert of grouped row i (offsets in LDS, ascending): largest e with off[e] <= i, or E
-// when i >= off[E].
-__device__ __forceinline__ int expert_of_row(const int* off, int E, int i) {
+// Expert of grouped row i (offsets ascending): largest e with off[e] <= i, or E when
+// i >= off[E].
+__device__ __forceinline__ int expert_of_row(const int32_t* off, int E, int i) {
   if (i >= off[E]) return E;
   int lo = 0, hi = E;  // off[lo] <= i < off[hi]
   while (hi - lo > 1) {
@@ -119,46 +61,48 @@ __device__ __forceinline__ int expert_of_row(const int* off, int E, int i) {
 }
 
 // ------------------------------------------------------------------------- SwiGLU
-// One wave per row i of acc13 [R, 2I]: h = bf16(silu(zg) * zu) with the gate / up globals
-// of the row's expert and the row's activation global.  Optionally writes h (bf16) and /
-// or quantizes h in place of a separate nvfp4_quantize_rows pass (same arithmetic).
-template <int BPL>
-__global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ acc13, int R, int I,
+// One workgroup per row i of acc13 [R, 2I]: h = bf16(silu(zg) * zu) with the gate / up
+// globals of the row's expert and the row's activation global.  Optionally writes h (bf16)
+// and / or quantizes h in place of a separate nvfp4_quantize_rows pass (same arithmetic).
+template <int BPT>
+__global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ acc13, int I,
                                                 const int32_t* __restrict__ offsets, int E,
                                                 const float* __restrict__ g_gate,
                                                 const float* __restrict__ g_up,
                                                 const float* __restrict__ row_gs,
+                                                const int32_t* __restrict__ gs_map,
                                                 uint16_t* __restrict__ h, uint8_t* __restrict__ q,
                                                 uint8_t* __restrict__ sc, float* __restrict__ h_gs) {
-  extern __shared__ int s_off[];
-  for (int k = threadIdx.x; k <= E; k += blockDim.x) s_off[k] = offsets[k];
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= R) return;
-  const int e = expert_of_row(s_off, E, row);
+  __shared__ float s_red[4];
+  const int row = blockIdx.x;
+  const int e = expert_of_row(offsets, E, row);  // uniform: scalar loads
   const int NB = I / 16;
-  float v[BPL][16];
+  float v[BPT][16];
   float cg = 0.0f, cu = 0.0f;
   if (e < E) {
-    const float gs = row_gs[row];
+    const float gs = row_gs[gs_map ? gs_map[row] : row];
     cg = gs * g_gate[e];
     cu = gs * g_up[e];
   }
 #pragma unroll
-  for (int k = 0; k < BPL; ++k) {
-    const int b = lane + 64 * k;
+  for (int k = 0; k < BPT; ++k) {
+    const int b = threadIdx.x + blockDim.x * k;
 #pragma unroll
     for (int x = 0; x < 16; ++x) v[k][x] = 0.0f;
     if (b >= NB || e >= E) continue;
     const f32x4* pg = (const f32x4*)(acc13 + (size_t)row * 2 * I + 16 * b);
     const f32x4* pu = (const f32x4*)(acc13 + (size_t)row * 2 * I + I + 16 * b);
+    f32x4 ag[4], au[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const f32x4 ag = pg[c], au = pu[c];
+      ag[c] = pg[c];
+      au[c] = pu[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const float zg = cg * ag[x], zu = cu * au[x];
+        const float zg = cg * ag[c][x], zu = cu * au[c][x];
         const float silu = zg / (1.0f + expf(-zg));
         v[k][4 * c + x] = __uint_as_float(f32_to_bf16_rne(silu * zu) << 16);  // bf16 value
       }
@@ -166,8 +110,8 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ acc13,
   }
   if (h) {
 #pragma unroll
-    for (int k = 0; k < BPL; ++k) {
-      const int b = lane + 64 * k;
+    for (int k = 0; k < BPT; ++k) {
+      const int b = threadIdx.x + blockDim.x * k;
       if (b >= NB) continue;
       u32x4 w[2];
 #pragma unroll
@@ -181,47 +125,54 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ acc13,
       p[1] = w[1];
     }
   }
-  if (q) quantize_row_regs<BPL>(v, NB, lane, q + (size_t)row * (I / 2), sc + (size_t)row * NB,
-                                h_gs + row);
+  if (q) {
+    const float amax = row_amax_threads<BPT>(v, threadIdx.x, blockDim.x, s_red);
+    quantize_row_store<BPT>(v, NB, threadIdx.x, blockDim.x, amax, q + (size_t)row * (I / 2),
+                            sc + (size_t)row * NB, h_gs + row);
+  }
 }
 
 hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* offsets, int E,
                          const float* g_gate, const float* g_up, const float* row_gs,
-                         uint16_t* h, uint8_t* q, uint8_t* sc, float* h_gs, hipStream_t s) {
+                         const int32_t* gs_map, uint16_t* h, uint8_t* q, uint8_t* sc, float* h_gs,
+                         hipStream_t s) {
   if (R == 0) return hipSuccess;
-  const dim3 grid((R + 3) / 4), block(256);
-  const size_t lds = sizeof(int) * (size_t)(E + 1);
-  switch (bpl_for(I / 16)) {
-    case 1: hipLaunchKernelGGL(k_swiglu<1>, grid, block, lds, s, acc13, R, I, offsets, E, g_gate, g_up, row_gs, h, q, sc, h_gs); break;
-    case 2: hipLaunchKernelGGL(k_swiglu<2>, grid, block, lds, s, acc13, R, I, offsets, E, g_gate, g_up, row_gs, h, q, sc, h_gs); break;
-    case 4: hipLaunchKernelGGL(k_swiglu<4>, grid, block, lds, s, acc13, R, I, offsets, E, g_gate, g_up, row_gs, h, q, sc, h_gs); break;
-    default: hipLaunchKernelGGL(k_swiglu<8>, grid, block, lds, s, acc13, R, I, offsets, E, g_gate, g_up, row_gs, h, q, sc, h_gs); break;
-  }
+  const int NB = I / 16, nt = row_threads(NB);
+  if (NB <= 256)
+    hipLaunchKernelGGL(k_swiglu<1>, dim3(R), dim3(nt), 0, s, acc13, I, offsets, E, g_gate, g_up,
+                       row_gs, gs_map, h, q, sc, h_gs);
+  else
+    hipLaunchKernelGGL(k_swiglu<2>, dim3(R), dim3(nt), 0, s, acc13, I, offsets, E, g_gate, g_up,
+                       row_gs, gs_map, h, q, sc, h_gs);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------- scatter
-// Grid (T, ceil(H / 256)); one wave per (token, 256 columns), 4 columns per lane.  The
-// token's rows are taken 64 at a time: each lane finds one row's expert and coefficient
-// row_w * g_down * row_gs, then the wave accumulates the rows in ascending order.
-__global__ __launch_bounds__(64) void k_scatter(const float* __restrict__ y, int H,
-                                                const int32_t* __restrict__ offsets, int E,
-                                                const float* __restrict__ row_w,
-                                                const float* __restrict__ g_down,
-                                                const float* __restrict__ row_gs,
-                                                const int32_t* __restrict__ tok_off,
-                                                const int32_t* __restrict__ tok_rows,
-                                                uint16_t* __restrict__ out) {
-  extern __shared__ int s_off[];
+// Grid (T, ceil(H / 256)), 8 waves per workgroup, 4 columns per lane.  Wave w sums the
+// token's rows p = tok_off[t] + w, + 8, ... in ascending order, each scaled by
+// row_w * g_down * row_gs (the coefficients of up to 64 rows are computed by the lanes in
+// parallel); the eight partial rows are then added in wave order.  The summation order
+// depends only on the token's row count, so a token's output does not depend on the
+// other tokens of the batch.
+constexpr int kScatterWaves = 8;
+
+__global__ __launch_bounds__(64 * kScatterWaves) void k_scatter(
+    const float* __restrict__ y, int H, const int32_t* __restrict__ offsets, int E,
+    const float* __restrict__ row_w, const float* __restrict__ g_down,
+    const float* __restrict__ row_gs, const int32_t* __restrict__ tok_off,
+    const int32_t* __restrict__ tok_rows, uint16_t* __restrict__ out) {
+  __shared__ f32x4 s_part[kScatterWaves][64];
+  extern __shared__ int32_t s_off[];  // expert offsets, for the row -> expert searches
   for (int k = threadIdx.x; k <= E; k += blockDim.x) s_off[k] = offsets[k];
   __syncthreads();
-  const int t = blockIdx.x, lane = threadIdx.x;
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = blockIdx.y * 256 + 4 * lane;
   const bool cv = col < H;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int p0 = tok_off[t], p1 = tok_off[t + 1];
-  for (int base = p0; base < p1; base += 64) {
-    const int p = base + lane;
+  for (int base = p0 + wave; base < p1; base += 64 * kScatterWaves) {
+    // rows base + 8k, k < 64: coefficients in parallel
+    const int p = base + kScatterWaves * lane;
     int i = 0;
     float c = 0.0f;
     if (p < p1) {
@@ -229,7 +180,8 @@ __global__ __launch_bounds__(64) void k_scatter(const float* __restrict__ y, int
       const int e = expert_of_row(s_off, E, i);
       c = (e < E) ? row_w[i] * g_down[e] * row_gs[i] : 0.0f;
     }
-    const int n = min(64, p1 - base);
+    const int n = min(64, (p1 - base + kScatterWaves - 1) / kScatterWaves);
+#pragma unroll 4
     for (int k = 0; k < n; ++k) {
       const int ik = __shfl(i, k, 64);
       const float ck = __shfl(c, k, 64);
@@ -242,11 +194,22 @@ __global__ __launch_bounds__(64) void k_scatter(const float* __restrict__ y, int
       }
     }
   }
-  if (cv) {
-    u32x2 o;
-    o[0] = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    o[1] = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-    *(u32x2*)(out + (size_t)t * H + col) = o;
+  s_part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && cv) {
+    f32x4 sum = s_part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kScatterWaves; ++w) {
+      const f32x4 o = s_part[w][lane];
+      sum[0] += o[0];
+      sum[1] += o[1];
+      sum[2] += o[2];
+      sum[3] += o[3];
+    }
+    u32x2 ov;
+    ov[0] = f32_to_bf16_rne(sum[0]) | (f32_to_bf16_rne(sum[1]) << 16);
+    ov[1] = f32_to_bf16_rne(sum[2]) | (f32_to_bf16_rne(sum[3]) << 16);
+    *(u32x2*)(out + (size_t)t * H + col) = ov;
   }
 }
 
@@ -256,10 +219,9 @@ hipError_t launch_scatter(const float* y, int R, int H, const int32_t* offsets, 
                           hipStream_t s) {
   (void)R;
   if (T == 0) return hipSuccess;
-  const dim3 grid(T, (H + 255) / 256), block(64);
-  const size_t lds = sizeof(int) * (size_t)(E + 1);
-  hipLaunchKernelGGL(k_scatter, grid, block, lds, s, y, H, offsets, E, row_w, g_down, row_gs,
-                     tok_off, tok_rows, out);
+  const dim3 grid(T, (H + 255) / 256), block(64 * kScatterWaves);
+  hipLaunchKernelGGL(k_scatter, grid, block, sizeof(int32_t) * (size_t)(E + 1), s, y, H, offsets, E,
+                     row_w, g_down, row_gs, tok_off, tok_rows, out);
   return hipGetLastError();
 }
 

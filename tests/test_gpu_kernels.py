@@ -125,7 +125,8 @@ def _run_group(B, x, S, H, a_expert, a_src, a_dst, a_w, E, T):
     return {k: host(v) for k, v in outs.items()}, err
 
 
-@pytest.mark.parametrize("case", ["random_invalid", "ragged570", "zipf", "empty", "one_expert"])
+@pytest.mark.parametrize("case", ["random_invalid", "ragged570", "zipf", "empty", "one_expert",
+                                  "many_experts", "ragged2303"])
 def test_group_gather_bit_exact(lib, case):
     from nvfp4_block_scaled_gather_amd import binding as B
     say("group", case)
@@ -151,6 +152,16 @@ def test_group_gather_bit_exact(lib, case):
     elif case == "empty":
         E, S, T, R = 8, 4, 4, 0
         a_expert = a_src = a_dst = np.zeros(0, np.int64)
+    elif case == "many_experts":      # key ranges too wide for per-wave histograms
+        E, S, T, R = 3000, 700, 50, 700
+        a_expert = rng.integers(-1, E + 1, R)
+        a_src = np.arange(R)
+        a_dst = rng.integers(0, T, R)
+    elif case == "ragged2303":
+        E, S, T, R = 288, 2303, 288, 2303
+        a_expert = np.repeat(np.arange(E), 1 + rng.multinomial(R - E, np.full(E, 1 / E)))
+        a_src = np.arange(R)
+        a_dst = rng.permutation(R) // 8
     else:
         E, S, T, R = 5, 3, 2, 100
         a_expert = np.full(R, 3)

@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--gemv-max-rows", type=int, default=None)
     p.add_argument("--kernel-iters", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-experts", type=int, default=24,
+    p.add_argument("--cpu-experts", type=int, default=144,
                    help="experts in the oracle's bounded sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy 3 times (reference for the HBM "
@@ -68,6 +68,30 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
                       "bytes_written_per_copy": n, "copies": 3}), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_w13_ragged570_hbm_bytes.txt")
+
+
+def measured_traffic(workload):
+    """HBM bytes per w13 grouped-GEMM launch from the committed profiler-counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or None when
+    the summary is for another workload or the GEMM sources changed since it was taken."""
+    from nvfp4_block_scaled_gather_amd import build as _b
+    try:
+        fields = dict(l.split(":", 1) for l in open(TRAFFIC_FILE).read().splitlines()
+                      if ":" in l and not l.startswith((" ", "#", "|")))
+    except OSError:
+        return None
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("workload") != workload:
+        return None
+    if fields.get("kernel_sources_sha256") != _b.kernel_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def time_layer(dl, steps, warmup):
@@ -135,9 +159,13 @@ def cpu_baseline(wl, n_experts):
     active = wl.active_experts()
     keep = set(active[:n_experts])
     sel = np.array([j for j in range(wl.R) if int(wl.a_expert[j]) in keep], dtype=np.int64)
+    # input generation (the seeded weights) stays outside the timed region
+    w13 = {e: wl.w13(e) for e in keep}
+    w2 = {e: wl.w2(e) for e in keep}
     t0 = time.perf_counter()
     omoe.layer_forward(wl.x, wl.a_expert[sel], wl.a_src[sel], wl.a_dst[sel], wl.a_w[sel], wl.T,
-                       wl.w13, wl.w2, wl.g_gate, wl.g_up, wl.g_down, wl.E, wl.H, wl.I)
+                       w13.__getitem__, w2.__getitem__, wl.g_gate, wl.g_up, wl.g_down,
+                       wl.E, wl.H, wl.I)
     dt = time.perf_counter() - t0
     nbytes = len(keep) * LAYER_BYTES_PER_EXPERT
     cpu_model = ""
@@ -151,7 +179,7 @@ def cpu_baseline(wl, n_experts):
     return {
         "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
         "sample": "%s: rows of the first %d of %d active experts (%d of %d expert-rows), whole "
-                  "layer in the numpy float64 oracle; %.2f s, extrapolates to %.0f ms per layer; "
+                  "layer in the numpy float64 oracle, weight generation excluded; %.2f s, extrapolates to %.0f ms per layer; "
                   "host %d logical CPUs (%s); numpy dequantization is single-threaded, BLAS "
                   "matrix-vector products use %d threads"
                   % (wl.name, len(keep), len(active), len(sel), wl.R, dt,
@@ -227,7 +255,7 @@ def main():
                  + R * 2 * I * 4)                                   # fp32 outputs
     achieved = alg_bytes / (res["w13_gemm_ms"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
                 "kernel": "grouped_gemm_nvfp4 (w13, N=4096, K=4096) on %s" % args.workload,
                 "bytes_per_launch": alg_bytes}
     cpu = None

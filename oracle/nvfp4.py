@@ -6,7 +6,7 @@ scales and an fp32 ``weight_scale_2`` global per projection):
 
 * element: e2m1 nibble — bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa;
 * block scale: one e4m3 byte per 16 consecutive elements along K.  The variant is the
-  OCP "e4m3fn" one: [MF] counts "126 finite positive e4m3 codes", which holds for
+  OCP "e4m3fn" one: [MF] gives the e4m3 grid 126 finite positive codes, which holds for
   e4m3fn (0x7F is NaN, max 448) and not for the FNUZ variant (127 codes, max 240);
 * global: one fp32 scale per row (activations) or per projection (weights).
 

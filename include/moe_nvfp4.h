@@ -75,12 +75,17 @@ enum { MOE_ERR_EXPERT = 1, MOE_ERR_SRC = 2, MOE_ERR_DST = 4 };
  * nvfp4_pack_weights: nib [E, N, K/2] canonical e2m1 bytes (row-major, even element in
  *   the low nibble), scl [E, N, K/16] e4m3 scale bytes (row-major) -> packed
  *   [nvfp4_packed_weight_bytes(E, N, K)] bytes, 16-byte aligned.  Values are unchanged:
- *   it is a byte permutation.  Because the packed form is a sequence of independent
- *   16-row tiles, packing a fused [2I, K] gate|up matrix gives the concatenation of the
- *   packed gate and up matrices whenever I % 16 == 0.
+ *   it is a byte permutation, except that a block whose scale is negative is stored with
+ *   the scale's magnitude and the signs of its 16 e2m1 codes flipped (the same 16 values
+ *   bit for bit, negative zero included), so that packed scales are never negative.
+ *   Because the packed form is a sequence of independent 16-row tiles, packing a fused
+ *   [2I, K] gate|up matrix gives the concatenation of the packed gate and up matrices
+ *   whenever I % 16 == 0.
  *   Limits: N % 16 == 0, K % 128 == 0, E >= 1.
  *
- * nvfp4_unpack_weights: exact inverse of nvfp4_pack_weights (same limits).
+ * nvfp4_unpack_weights: inverse of nvfp4_pack_weights (same limits): returns the packed
+ *   bytes in canonical order — the original bytes when no block scale was negative, else
+ *   the value-identical form described above.
  * ---------------------------------------------------------------------------------- */
 size_t nvfp4_packed_weight_bytes(int E, int N, int K);
 int nvfp4_pack_weights(const uint8_t* nib, const uint8_t* scl, int E, int N, int K,

@@ -61,23 +61,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // The gfx950 scaled FP4 conversion applies only the exponent of its fp32 scale operand,
 // so it cannot apply an e4m3 block scale (4 significant bits) by itself.  We convert
 // with a power-of-two scale of 2^8 and multiply by the block scale expressed as f16
-// times 2^-8: the e4m3fn byte with its exponent field re-read as f16 bits
-// ((b & 0x7F) << 7) is exactly e4m3 * 2^-8 for normal and subnormal codes alike.
-// Every product e2m1 * e4m3 (6 significant bits, magnitude in [2^-10, 2688]) is exact
-// in f16, so the dequantized operands are exact.
-__device__ __forceinline__ uint32_t e4m3_to_f16x2_scaled(uint32_t b) {
-  const uint32_t h = ((b & 0x7Fu) << 7) | ((b & 0x80u) << 8);
-  return h | (h << 16);
+// times 2^-8: an e4m3fn byte s.eeee.mmm placed as f16 bits s.0eeee.mmm0000000 is exactly
+// e4m3 * 2^-8, for normal and subnormal codes alike.  Every product e2m1 * e4m3 (6
+// significant bits, magnitude in [2^-10, 2688]) is exact in f16, so the dequantized
+// operands are exact.
+//
+// Scales travel in pairs: the two block scales of a lane's 32-element row segment, as the
+// f16 values of both in one 32-bit register (first block in the low half); a multiply
+// broadcasts the half it needs.
+
+// Scale pair from two e4m3 bytes of `w` (selector: which bytes; 0x0c010c00 takes bytes
+// 0 and 1, 0x0c030c02 bytes 2 and 3) whose sign bits are clear: the f16 bits are the byte
+// shifted left by 7.  Packed weight scales are always non-negative (the packer moves a
+// negative scale's sign into the block's e2m1 codes).
+__device__ __forceinline__ uint32_t scale_pair_pos(uint32_t w, uint32_t sel) {
+  return __builtin_amdgcn_perm(0u, w, sel) << 7;
+}
+// Same for bytes 0 and 1 of `w` that may carry a sign: the sign bit moves to bit 15.
+__device__ __forceinline__ uint32_t scale_pair_signed(uint32_t w) {
+  const uint32_t u = __builtin_amdgcn_perm(0u, w, 0x0c010c00u) << 7;
+  return (u & 0x3F803F80u) | ((u << 1) & 0x80008000u);
 }
 
 // Eight e2m1 nibbles (one 32-bit word, element 2k in the low nibble of byte k) times
-// the packed f16 scale pair -> 8 exact f16 values in element order.
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, uint32_t scale_pair) {
+// one scale of a pair (hi: the second block's) -> 8 exact f16 values in element order.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, uint32_t pair, bool hi) {
   f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0);
   f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1);
   f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2);
   f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
-  const f16x2 s = __builtin_bit_cast(f16x2, scale_pair);
+  const f16x2 h = __builtin_bit_cast(f16x2, pair);
+  const f16x2 s = hi ? __builtin_shufflevector(h, h, 1, 1) : __builtin_shufflevector(h, h, 0, 0);
   p0 *= s; p1 *= s; p2 *= s; p3 *= s;
   f16x8 r;
   r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
@@ -94,17 +108,27 @@ __device__ __forceinline__ void e2m1x8_to_f16(uint32_t w, f16x2 out[4]) {
 }
 
 // ------------------------------------------------------------------ packed weight layout
-// A matrix [N, K] is stored as N/16 tiles of 16 rows; a tile is K/128 chunks of 128
-// columns, and a chunk is 1152 contiguous bytes:
-//   [0, 1024):    lane l (0..63) owns bytes [16l, 16l + 16): row (l & 15) of the tile,
-//                 columns [128c + 32(l >> 4), +32) — the canonical nibble bytes of that
-//                 row segment, in order;
-//   [1024, 1152): lane l owns bytes [1024 + 2l, +2): the two e4m3 scale bytes of that
-//                 same 32-column row segment.
-// So one wave reads a tile's chunk with one 16-byte and one 2-byte load per lane, both
-// perfectly coalesced.  A tile is 9K bytes and an expert N/16 consecutive tiles; there
-// is no padding (N * K * 9/16 bytes per expert).
+// A matrix [N, K] is stored as N/16 tiles of 16 rows, an expert as N/16 consecutive tiles,
+// with no padding (N * K * 9/16 bytes per expert).  A tile covers K/128 chunks of 128
+// columns, taken in scale groups of S consecutive chunks (S = scale_group(K/128): the
+// largest of 8, 4, 2, 1 that divides K/128).  A scale group is S * 1152 contiguous bytes:
+//   [j * 1024, (j + 1) * 1024), j < S: chunk j of the group; lane l (0..63) owns bytes
+//                 [16l, 16l + 16): row (l & 15) of the tile, columns [128c + 32(l >> 4), +32)
+//                 of the chunk's 128 columns c — the canonical nibble bytes of that row
+//                 segment, in order;
+//   [S * 1024 + 2S * l, +2S): lane l's scale bytes for the S chunks of the group, two
+//                 per chunk (the two e4m3 scales of its 32-column row segment), chunk by
+//                 chunk.
+// Block scales are stored non-negative: a block whose scale byte has the sign bit set is
+// stored with that bit clear and the sign bits of its 16 e2m1 codes flipped, which gives
+// the same 16 values bit for bit (negative zero included).
+// So a wave reads a chunk of a tile with one 16-byte load per lane, and the scales of S
+// chunks with one 2S-byte load per lane (16 bytes at S = 8), all perfectly coalesced.
 constexpr int kChunkBytes = 1152;
+
+__host__ __device__ __forceinline__ int scale_group(int nc) {
+  return nc % 8 == 0 ? 8 : nc % 4 == 0 ? 4 : nc % 2 == 0 ? 2 : 1;
+}
 
 // ------------------------------------------------------------------ row quantization
 __device__ __forceinline__ float wave_max(float v) {

@@ -2,30 +2,31 @@
 // non-empty expert group e (alpha = 1; the globals are applied by the next kernel).
 //
 // The GEMM is weight-stream bound: every active expert's packed weights are read from HBM
-// exactly once, with one 16-byte (nibbles) and one 2-byte (scales) load per lane per
-// 16-row tile per 128-column chunk — 1152 contiguous bytes per wave — and a ring of D
-// chunks in flight per wave.
+// exactly once.  Per 16-row tile, a wave reads each 128-column chunk with one 16-byte load
+// per lane and the scales of a group of up to 8 chunks with one load of up to 16 bytes per
+// lane (layout in common.h), keeping a ring of D chunks in flight.
 //
-// Work decomposition: a work item is (expert, 4 * NS consecutive 16-row tiles); each of
-// the 4 waves of a workgroup streams NS tiles over all of K.  A persistent grid walks the
-// items round-robin, so workgroups differ by at most one item.
+// Work decomposition: a work item is (expert, 4 * NS consecutive 16-row tiles) and one
+// workgroup runs one item; each of its 4 waves streams NS tiles over all of K.  The
+// group's activation rows are staged once per workgroup in LDS (direct buffer-to-LDS
+// loads, up to 16 rows per pass), so the four waves share them and the vector-memory path
+// carries only the weight stream.
 //
 // Two kernels, each over the groups its path owns (chosen per group on the device, so
 // the host never needs the group sizes):
 //  * k_gemm_mfma: the weight tile is the A operand of v_mfma_f32_16x16x32_f16 (16 weight
-//    rows x 32 k), the group's activation rows the B operand (16 columns, zero-padded),
-//    CT column tiles (16 * CT rows) per pass.  Lane l holds weight row l & 15 and the 32
-//    k of quarter l >> 4 of each 128-column chunk; MFMA j of the chunk takes word j
-//    (8 k) of that quarter, and the B operand uses the same k assignment.
-//  * k_gemm_gemv (groups of at most 4 rows): each lane dots its weight row segment with
-//    each activation row's matching segment, 16 elements (one scale block) at a time with
-//    v_dot2_f32_f16, then multiplies by the weight block scale; the four k-quarters are
-//    summed across lanes at the end in a fixed tree.
+//    rows x 32 k), the pass's activation rows the B operand (16 columns).  Lane l holds
+//    weight row l & 15 and the 32 k of quarter l >> 4 of each 128-column chunk; MFMA j of
+//    the chunk takes word j (8 k) of that quarter, and the B operand uses the same k
+//    assignment.  A B column beyond the pass's rows only feeds an output row that is not
+//    stored, so those lanes simply re-read row 0.
+//  * k_gemm_gemv (groups of at most 4 rows per pass): each lane dots its weight row
+//    segment with each activation row's matching segment, 16 elements (one scale block)
+//    at a time with v_dot2_f32_f16, then multiplies by the weight block scale; the four
+//    k-quarters are summed across lanes at the end in a fixed tree.
 // Both dequantize exactly (dequant8 in common.h) and accumulate in fp32 in an order that
 // depends only on (N, K) and the path, never on the other rows of the group.
 #include "common.h"
-
-#include <mutex>
 
 #ifndef MOE_GEMM_NS
 #define MOE_GEMM_NS 2  // 16-row tiles per wave, MFMA kernel
@@ -33,23 +34,21 @@
 #ifndef MOE_GEMM_D
 #define MOE_GEMM_D 4   // chunks in flight per wave, MFMA kernel
 #endif
-#ifndef MOE_GEMM_CT
-#define MOE_GEMM_CT 1  // 16-row activation column tiles per MFMA pass
-#endif
 #ifndef MOE_GEMV_NS
 #define MOE_GEMV_NS 2  // 16-row tiles per wave, GEMV kernel
 #endif
 #ifndef MOE_GEMV_D
 #define MOE_GEMV_D 2
 #endif
-#ifndef MOE_GEMM_WGS_PER_CU
-#define MOE_GEMM_WGS_PER_CU 0  // 0: one work item per workgroup; n > 0: persistent, n per CU
+#ifndef MOE_W_CPOL
+#define MOE_W_CPOL 2  // cache policy of the weight-stream loads: non-temporal (read once)
 #endif
 
 namespace moe {
 
 constexpr int kGemmWaves = 4;
-constexpr int kGemvRows = 4;
+constexpr int kPassRows = 16;  // activation rows per MFMA pass (the B operand's columns)
+constexpr int kGemvRows = 4;   // activation rows per GEMV pass
 
 struct GemmArgs {
   const uint8_t* aq;     // activation rows [A, K/2] (A = a_rows)
@@ -64,10 +63,15 @@ struct GemmArgs {
   int gmin, gmax;  // this kernel's groups: gmin <= G <= gmax
 };
 
-// Activation row of grouped row i (i < rows of the pass); -1 when the lane has no row.
-__device__ __forceinline__ int act_row(const GemmArgs& p, int i, bool valid) {
-  if (!valid) return -1;
-  return p.amap ? p.amap[i] : i;
+// ------------------------------------------------------------------------- LDS layout
+// [E x uint16 active-expert list, padded to 16 B][rows x q_stride nibbles][rows x s_stride
+// scales].  The row strides are padded so that the 16 rows a wave reads at once fall in
+// distinct banks (a nibble row stride of 16 mod 256 bytes, a scale row stride of 8 mod 256).
+__host__ __device__ __forceinline__ int act_list_bytes(int E) { return (2 * E + 15) & ~15; }
+__host__ __device__ __forceinline__ int q_stride(int K) { return K / 2 + 16; }
+__host__ __device__ __forceinline__ int s_stride(int K) { return K / 16 + 8; }
+static size_t gemm_lds_bytes(int E, int K, int rows) {
+  return (size_t)act_list_bytes(E) + (size_t)rows * (q_stride(K) + s_stride(K));
 }
 
 // Ids of the experts whose group size is in [gmin, gmax], ascending, into LDS (wave 0).
@@ -95,120 +99,199 @@ __device__ __forceinline__ int build_active_list(const GemmArgs& p, uint16_t* s_
     if (lane == 0) *s_nact = n;
   }
   __syncthreads();
-  return *s_nact;
+  return __builtin_amdgcn_readfirstlane(*s_nact);
 }
 
-// Buffer resource over [base, base + bytes): loads at offsets beyond the range return 0,
-// which zero-fills the activation rows a pass does not own without any branch.
+// Buffer resource over [base, base + bytes): loads at offsets beyond the range return 0
+// and touch no memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-#ifndef MOE_W_CPOL
-#define MOE_W_CPOL 2  // cache policy of the weight-stream loads: non-temporal (read once)
-#endif
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// ------------------------------------------------------------------------- MFMA path
-// One pass over K for NS weight tiles (wt: first tile, uniform) and CT activation column
-// tiles (rows arow0 .. arow0 + nrows - 1).  NC % D == 0.
-template <int NS, int D, int CT>
-__device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
-                                          int nsv, int arow0, int nrows, int col0) {
+// Stage activation rows arow0 .. arow0 + nrows - 1 (through amap) into LDS with
+// buffer-to-LDS loads: wave w copies rows w, w + 4, ...; a row is K/2 nibble bytes in
+// 1 KiB pieces (16 bytes per lane) and K/16 scale bytes in 256-byte pieces (4 bytes per
+// lane).  The caller waits for the loads and synchronizes before reading.
+__device__ __forceinline__ void stage_rows(const GemmArgs& p, int arow0, int nrows, uint8_t* s_q,
+                                           uint8_t* s_s) {
   const int lane = threadIdx.x & 63;
-  const int kq = lane >> 4, r = lane & 15;
-  const int K = p.K, NC = K / 128;
-  const int tstride = NC * kChunkBytes;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, nsv * tstride);
-  const int abytes = p.a_rows * (K / 2), sbytes = p.a_rows * (K / 16);
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, abytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, sbytes);
-  const int vw = 16 * lane, vws = 1024 + 2 * lane;
-  int va[CT], vs[CT];  // lanes without a row point past the end: their loads return 0
-#pragma unroll
-  for (int a = 0; a < CT; ++a) {
-    const int row = act_row(p, arow0 + 16 * a + r, 16 * a + r < nrows);
-    va[a] = row >= 0 ? row * (K / 2) + 16 * kq : abytes;
-    vs[a] = row >= 0 ? row * (K / 16) + 2 * kq : sbytes;
-  }
-
-  u32x4 wn[D][NS];
-  uint32_t ws[D][NS];
-  u32x4 an[D][CT];
-  uint32_t asc[D][CT];
-  f32x4 acc[NS][CT];
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int a = 0; a < CT; ++a) acc[s][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto load = [&](int c, int slot) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int so = s * tstride + c * kChunkBytes;
-      wn[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(wr, vw, so, MOE_W_CPOL);
-      ws[slot][s] = __builtin_amdgcn_raw_buffer_load_b16(wr, vws, so, MOE_W_CPOL);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qb = p.K / 2, sb = p.K / 16;
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, p.a_rows * qb);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, p.a_rows * sb);
+  for (int row = wave; row < nrows; row += kGemmWaves) {
+    const int i = arow0 + row;
+    const int src = __builtin_amdgcn_readfirstlane(p.amap ? p.amap[i] : i);
+    uint8_t* dq = s_q + row * q_stride(p.K);
+    uint8_t* ds = s_s + row * s_stride(p.K);
+    for (int o = 0; o < qb; o += 1024) {
+      if (o + 16 * lane < qb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(dq + o), 16, 16 * lane,
+                                                 src * qb + o, 0, 0);
     }
-#pragma unroll
-    for (int a = 0; a < CT; ++a) {
-      an[slot][a] = __builtin_amdgcn_raw_buffer_load_b128(ar, va[a], 64 * c, 0);
-      asc[slot][a] = __builtin_amdgcn_raw_buffer_load_b16(sr, vs[a], 8 * c, 0);
-    }
-  };
-
-#pragma unroll
-  for (int d = 0; d < D; ++d) load(d, d);
-
-  for (int c0 = 0; c0 < NC; c0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      f16x8 bop[CT][4];
-#pragma unroll
-      for (int a = 0; a < CT; ++a) {
-        const uint32_t s0 = e4m3_to_f16x2_scaled(asc[d][a] & 0xFFu);
-        const uint32_t s1 = e4m3_to_f16x2_scaled(asc[d][a] >> 8);
-        bop[a][0] = dequant8(an[d][a][0], s0);
-        bop[a][1] = dequant8(an[d][a][1], s0);
-        bop[a][2] = dequant8(an[d][a][2], s1);
-        bop[a][3] = dequant8(an[d][a][3], s1);
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint32_t w0 = e4m3_to_f16x2_scaled(ws[d][s] & 0xFFu);
-        const uint32_t w1 = e4m3_to_f16x2_scaled(ws[d][s] >> 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x8 aop = dequant8(wn[d][s][j], j < 2 ? w0 : w1);
-#pragma unroll
-          for (int a = 0; a < CT; ++a)
-            acc[s][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[a][j], acc[s][a], 0, 0, 0);
-        }
-      }
-      if (c0 + d + D < NC) load(c0 + d + D, d);
-    }
-  }
-
-  // lane l holds out rows (16a + r) x weight rows 4 kq .. 4 kq + 3 of each tile
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (s >= nsv) break;
-#pragma unroll
-    for (int a = 0; a < CT; ++a) {
-      if (16 * a + r < nrows) {
-        const int row = arow0 + 16 * a + r;
-        *(f32x4*)(p.out + (size_t)row * p.N + col0 + 16 * s + 4 * kq) = acc[s][a];
-      }
+    for (int o = 0; o < sb; o += 256) {
+      if (o + 4 * lane < sb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(ds + o), 4, 4 * lane,
+                                                 src * sb + o, 0, 0);
     }
   }
 }
 
-// Item loop shared by both kernels: item -> (expert, first tile of this wave).
+// The 2S scale bytes of one scale group for this lane (voff: its byte offset in the group).
+template <int S>
+__device__ __forceinline__ u32x4 load_scale_group(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if constexpr (S == 8) {
+    v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, MOE_W_CPOL);
+  } else if constexpr (S == 4) {
+    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, MOE_W_CPOL);
+    v[0] = t[0];
+    v[1] = t[1];
+  } else if constexpr (S == 2) {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, MOE_W_CPOL);
+  } else {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, MOE_W_CPOL);
+  }
+  return v;
+}
+
+// The two scale bytes of chunk j of a group (low byte: the first 16 of the 32 columns).
+__device__ __forceinline__ uint32_t chunk_scales(const u32x4& g, int j) {
+  return (g[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+}
+
+// ------------------------------------------------------------------------- weight ring
+// Streams NS tiles (buffer wr, tiles tstride bytes apart) over all of K in scale groups of
+// S chunks with a ring of D chunks (D <= S, both powers of two, S divides NC = K / 128).
+// consume(c, j, wn, sg) uses chunk c (chunk j of its group): wn[s] holds its nibbles for
+// tile s and sg[s] the group's scales.  Loads in the main loop are unconditional and
+// pinned right after the use of their slot, so every wait is a counted one and the
+// prefetch distance stays D chunks.
+template <int NS, int D, int S, class Consume>
+__device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC, int tstride,
+                                               int vw, int vs, Consume consume) {
+  u32x4 wn[D][NS];
+  u32x4 cur[NS], nxt[NS];
+  auto load_nib = [&](int c, int slot) {
+    const int g = c / S, j = c - g * S;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      wn[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(
+          wr, vw, s * tstride + g * S * kChunkBytes + j * 1024, MOE_W_CPOL);
+  };
+  auto load_scales = [&](int g, u32x4 (&sg)[NS]) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      sg[s] = load_scale_group<S>(wr, vs, s * tstride + g * S * kChunkBytes);
+  };
+  const int NG = NC / S;
+  load_scales(0, cur);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load_nib(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int g = 0;
+  for (; g + 1 < NG; ++g) {
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+      consume(g * S + j, j, wn[j % D], cur);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j == S - D) load_scales(g + 1, nxt);  // with the first refill of the next group
+      load_nib(g * S + j + D, j % D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) cur[s] = nxt[s];
+  }
+#pragma unroll
+  for (int j = 0; j < S; ++j) {  // last group: refill only inside it
+    consume(g * S + j, j, wn[j % D], cur);
+    if (j + D < S) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_nib(g * S + j + D, j % D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------- MFMA path
+// One pass: stage the pass's rows, then stream NS weight tiles (wt: first tile, uniform)
+// against them.  Every wave of the workgroup calls this together (it synchronizes); a
+// wave with no tile in this item (nsv <= 0) loads nothing (empty buffer range) and stores
+// nothing.
+template <int NS, int D, int S>
+__device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
+                                          int nsv, int arow0, int nrows, int col0,
+                                          uint8_t* s_q, uint8_t* s_s) {
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, r = lane & 15;
+  const int K = p.K, NC = K / 128;
+  // Passes of one item load the same weight chunks; keep the compiler from hoisting those
+  // loads out of the pass loop (it would hold a second copy of the ring in registers).
+  asm volatile("" ::: "memory");
+  const int tstride = NC * kChunkBytes;
+  // (readfirstlane: the clamp may be computed on the vector unit, and a descriptor the
+  // compiler believes divergent turns every load into a loop over lanes)
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(wt, __builtin_amdgcn_readfirstlane((nsv > 0 ? nsv : 0) * tstride));
+
+  stage_rows(p, arow0, nrows, s_q, s_s);
+  __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
+  __syncthreads();
+
+  const int rl = r < nrows ? r : 0;
+  const uint8_t* aq_l = s_q + rl * q_stride(K) + 16 * kq;
+  const uint8_t* as_l = s_s + rl * s_stride(K) + 2 * kq;
+  f32x4 acc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The B operand of chunk c is read from LDS while chunk c - 1 is computed (reads one
+  // chunk past the end land in the row padding or the next region: never used).
+  u32x4 an_next = *(const u32x4*)aq_l;
+  uint32_t asc_next = *(const uint16_t*)as_l;
+  stream_weights<NS, D, S>(wr, NC, tstride, 16 * lane, S * 1024 + 2 * S * lane,
+                           [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
+    const u32x4 an = an_next;
+    const uint32_t asc = asc_next;
+    an_next = *(const u32x4*)(aq_l + 64 * (c + 1));
+    asc_next = *(const uint16_t*)(as_l + 8 * (c + 1));
+    __builtin_amdgcn_sched_barrier(0);  // issue the reads before this chunk's work
+    const uint32_t sa = scale_pair_signed(asc);
+    f16x8 bop[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bop[q] = dequant8(an[q], sa, q >= 2);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint32_t sw = scale_pair_pos(sg[s][j >> 1], (j & 1) ? 0x0c030c02u : 0x0c010c00u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f16x8 aop = dequant8(wn[s][q], sw, q >= 2);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[q], acc[s], 0, 0, 0);
+      }
+    }
+  });
+
+  // lane l holds out row r x weight rows 4 kq .. 4 kq + 3 of each tile
+  if (r < nrows) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s < nsv)
+        *(f32x4*)(p.out + (size_t)(arow0 + r) * p.N + col0 + 16 * s + 4 * kq) = acc[s];
+    }
+  }
+}
+
+// Item -> (expert, first tile of this wave).
 struct ItemLoop {
-  int nact, items_per_e, total, tiles, per_item;
+  int items_per_e, total, tiles, per_item;
 };
 
 __device__ __forceinline__ ItemLoop item_loop(const GemmArgs& p, int nact, int NS) {
   ItemLoop L;
-  L.nact = nact;
   L.tiles = p.N / 16;
   L.per_item = kGemmWaves * NS;
   L.items_per_e = (L.tiles + L.per_item - 1) / L.per_item;
@@ -216,109 +299,89 @@ __device__ __forceinline__ ItemLoop item_loop(const GemmArgs& p, int nact, int N
   return L;
 }
 
-template <int NS, int D, int CT>
+template <int NS, int D, int S>
 __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
-  extern __shared__ uint16_t s_act[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_nact;
+  uint16_t* s_act = (uint16_t*)smem;
   const int nact = build_active_list(p, s_act, &s_nact);
+  uint8_t* s_q = smem + act_list_bytes(p.E);
+  uint8_t* s_s = s_q + kPassRows * q_stride(p.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const ItemLoop L = item_loop(p, nact, NS);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
-  for (int it = blockIdx.x; it < L.total; it += gridDim.x) {
+  for (int it = blockIdx.x; it < L.total; it += gridDim.x) {  // uniform over the workgroup
     const int e = __builtin_amdgcn_readfirstlane(s_act[it / L.items_per_e]);
     const int t0 = (it % L.items_per_e) * L.per_item + wave * NS;
     const int nsv = min(NS, L.tiles - t0);
-    if (nsv <= 0) continue;
     const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
     const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
-    const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)t0 * tile_bytes;
-    for (int b = 0; b < G; b += 16 * CT)
-      mfma_pass<NS, D, CT>(p, wt, nsv, r0 + b, min(16 * CT, G - b), 16 * t0);
+    const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+    for (int b = 0; b < G; b += kPassRows) {
+      __syncthreads();  // the previous pass is done with the staged rows
+      mfma_pass<NS, D, S>(p, wt, nsv, r0 + b, min(kPassRows, G - b), 16 * t0, s_q, s_s);
+    }
   }
 }
 
 // ------------------------------------------------------------------------- GEMV path
-template <int NS, int D>
+template <int NS, int D, int S>
 __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
-                                          int nsv, int arow0, int nrows, int col0) {
+                                          int nsv, int arow0, int nrows, int col0,
+                                          uint8_t* s_q, uint8_t* s_s) {
   constexpr int NR = kGemvRows;
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4;
   const int K = p.K, NC = K / 128;
+  asm volatile("" ::: "memory");  // no hoisting of this pass's weight loads (see mfma_pass)
   const int tstride = NC * kChunkBytes;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, nsv * tstride);
-  const int abytes = p.a_rows * (K / 2), sbytes = p.a_rows * (K / 16);
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, abytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, sbytes);
-  const int vw = 16 * lane, vws = 1024 + 2 * lane;
-  int va[NR], vs[NR];
-#pragma unroll
-  for (int a = 0; a < NR; ++a) {
-    const int row = act_row(p, arow0 + a, a < nrows);
-    va[a] = row >= 0 ? row * (K / 2) + 16 * kq : abytes;
-    vs[a] = row >= 0 ? row * (K / 16) + 2 * kq : sbytes;
-  }
+  // (readfirstlane: the clamp may be computed on the vector unit, and a descriptor the
+  // compiler believes divergent turns every load into a loop over lanes)
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(wt, __builtin_amdgcn_readfirstlane((nsv > 0 ? nsv : 0) * tstride));
 
-  u32x4 wn[D][NS];
-  uint32_t ws[D][NS];
-  u32x4 an[D][NR];
-  uint32_t asc[D][NR];
+  stage_rows(p, arow0, nrows, s_q, s_s);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
   float acc[NS][NR];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int a = 0; a < NR; ++a) acc[s][a] = 0.f;
 
-  auto load = [&](int c, int slot) {
+  stream_weights<NS, D, S>(wr, NC, tstride, 16 * lane, S * 1024 + 2 * S * lane,
+                           [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int so = s * tstride + c * kChunkBytes;
-      wn[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(wr, vw, so, MOE_W_CPOL);
-      ws[slot][s] = __builtin_amdgcn_raw_buffer_load_b16(wr, vws, so, MOE_W_CPOL);
-    }
+      const uint32_t ws = chunk_scales(sg[s], j);
+      const float sw0 = e4m3_to_f32(ws & 0xFFu), sw1 = e4m3_to_f32(ws >> 8);
+      f16x2 wv[16];
 #pragma unroll
-    for (int a = 0; a < NR; ++a) {
-      an[slot][a] = __builtin_amdgcn_raw_buffer_load_b128(ar, va[a], 64 * c, 0);
-      asc[slot][a] = __builtin_amdgcn_raw_buffer_load_b16(sr, vs[a], 8 * c, 0);
-    }
-  };
-
+      for (int q = 0; q < 4; ++q) e2m1x8_to_f16(wn[s][q], &wv[4 * q]);
 #pragma unroll
-  for (int d = 0; d < D; ++d) load(d, d);
-
-  for (int c0 = 0; c0 < NC; c0 += D) {
+      for (int a = 0; a < NR; ++a) {
+        if (a >= nrows) break;  // uniform
+        const u32x4 an = *(const u32x4*)(s_q + a * q_stride(K) + 16 * kq + 64 * c);
+        const uint32_t asc = *(const uint16_t*)(s_s + a * s_stride(K) + 2 * kq + 8 * c);
+        const uint32_t sa = scale_pair_signed(asc);
+        float b0 = 0.f, b1 = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+        for (int q = 0; q < 4; ++q) {
+          const f16x8 v = dequant8(an[q], sa, q >= 2);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const float sw0 = e4m3_to_f32(ws[d][s] & 0xFFu), sw1 = e4m3_to_f32(ws[d][s] >> 8);
-        f16x2 wv[16];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) e2m1x8_to_f16(wn[d][s][j], &wv[4 * j]);
-#pragma unroll
-        for (int a = 0; a < NR; ++a) {
-          if (a >= nrows) break;  // uniform
-          const uint32_t s0 = e4m3_to_f16x2_scaled(asc[d][a] & 0xFFu);
-          const uint32_t s1 = e4m3_to_f16x2_scaled(asc[d][a] >> 8);
-          float b0 = 0.f, b1 = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f16x8 v = dequant8(an[d][a][j], j < 2 ? s0 : s1);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const f16x2 x2 = f16x2{v[2 * m], v[2 * m + 1]};
-              if (j < 2) b0 = __builtin_amdgcn_fdot2(wv[4 * j + m], x2, b0, false);
-              else b1 = __builtin_amdgcn_fdot2(wv[4 * j + m], x2, b1, false);
-            }
+          for (int m = 0; m < 4; ++m) {
+            const f16x2 x2 = f16x2{v[2 * m], v[2 * m + 1]};
+            if (q < 2) b0 = __builtin_amdgcn_fdot2(wv[4 * q + m], x2, b0, false);
+            else b1 = __builtin_amdgcn_fdot2(wv[4 * q + m], x2, b1, false);
           }
-          acc[s][a] = fmaf(sw0, b0, acc[s][a]);
-          acc[s][a] = fmaf(sw1, b1, acc[s][a]);
         }
+        acc[s][a] = fmaf(sw0, b0, acc[s][a]);
+        acc[s][a] = fmaf(sw1, b1, acc[s][a]);
       }
-      if (c0 + d + D < NC) load(c0 + d + D, d);
     }
-  }
+  });
 
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -333,11 +396,14 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
   }
 }
 
-template <int NS, int D>
+template <int NS, int D, int S>
 __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
-  extern __shared__ uint16_t s_act[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_nact;
+  uint16_t* s_act = (uint16_t*)smem;
   const int nact = build_active_list(p, s_act, &s_nact);
+  uint8_t* s_q = smem + act_list_bytes(p.E);
+  uint8_t* s_s = s_q + kGemvRows * q_stride(p.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const ItemLoop L = item_loop(p, nact, NS);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
@@ -346,71 +412,63 @@ __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
     const int e = __builtin_amdgcn_readfirstlane(s_act[it / L.items_per_e]);
     const int t0 = (it % L.items_per_e) * L.per_item + wave * NS;
     const int nsv = min(NS, L.tiles - t0);
-    if (nsv <= 0) continue;
     const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
     const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
-    const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)t0 * tile_bytes;
-    for (int b = 0; b < G; b += kGemvRows)
-      gemv_pass<NS, D>(p, wt, nsv, r0 + b, min(kGemvRows, G - b), 16 * t0);
+    const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+    for (int b = 0; b < G; b += kGemvRows) {
+      __syncthreads();
+      gemv_pass<NS, D, S>(p, wt, nsv, r0 + b, min(kGemvRows, G - b), 16 * t0, s_q, s_s);
+    }
   }
 }
 
 // ------------------------------------------------------------------------- launch
-static hipError_t cu_count(int* cus) {
-  static std::mutex mu;
-  static int cache[64] = {0};
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> g(mu);
-  if (!cache[dev]) {
-    int c = 0;
-    err = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    cache[dev] = c > 0 ? c : 1;
-  }
-  *cus = cache[dev];
-  return hipSuccess;
-}
-
-// Workgroups to launch: every possible item (inactive ones exit after the prologue), or a
-// persistent grid of MOE_GEMM_WGS_PER_CU workgroups per CU.
-static int gemm_grid(int per_item, const GemmArgs& a, int cus) {
+// One workgroup per possible item (workgroups past the active items exit after building
+// the active list).
+static int gemm_grid(int per_item, const GemmArgs& a) {
   const long items_per_e = (a.N / 16 + per_item - 1) / per_item;
-  const long max_items = items_per_e * a.E;
-  if (MOE_GEMM_WGS_PER_CU <= 0) return (int)max_items;
-  const long slots = (long)MOE_GEMM_WGS_PER_CU * cus;
-  return (int)(max_items < slots ? max_items : slots);
+  return (int)(items_per_e * a.E);
 }
 
-// Ring depth: the configured depth, reduced until it divides the chunk count K / 128.
-static int ring_depth(int K, int dmax) {
-  const int nc = K / 128;
-  int d = dmax;
-  while (d > 1 && nc % d) d >>= 1;
-  return d;
+template <class Kern>
+static hipError_t launch_one(Kern kern, int per_item, const GemmArgs& a, int rows, hipStream_t s) {
+  const size_t lds = gemm_lds_bytes(a.E, a.K, rows);
+  if (lds > 65536) {
+    const hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(kern, dim3(gemm_grid(per_item, a)), dim3(256), lds, s, a);
+  return hipGetLastError();
 }
 
-template <int D>
-static void launch_mfma_d(const GemmArgs& a, int cus, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_mfma<MOE_GEMM_NS, D, MOE_GEMM_CT>),
-                     dim3(gemm_grid(kGemmWaves * MOE_GEMM_NS, a, cus)), dim3(256), lds, s, a);
+// The packed layout's scale group S fixes the kernel instance; the ring depth is the
+// configured one, capped at S.
+static hipError_t launch_mfma(const GemmArgs& a, hipStream_t s) {
+  const int per = kGemmWaves * MOE_GEMM_NS;
+  constexpr int D = MOE_GEMM_D;
+  switch (scale_group(a.K / 128)) {
+    case 8: return launch_one(k_gemm_mfma<MOE_GEMM_NS, (D < 8 ? D : 8), 8>, per, a, kPassRows, s);
+    case 4: return launch_one(k_gemm_mfma<MOE_GEMM_NS, (D < 4 ? D : 4), 4>, per, a, kPassRows, s);
+    case 2: return launch_one(k_gemm_mfma<MOE_GEMM_NS, (D < 2 ? D : 2), 2>, per, a, kPassRows, s);
+    default: return launch_one(k_gemm_mfma<MOE_GEMM_NS, 1, 1>, per, a, kPassRows, s);
+  }
 }
 
-template <int D>
-static void launch_gemv_d(const GemmArgs& a, int cus, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_gemv<MOE_GEMV_NS, D>),
-                     dim3(gemm_grid(kGemmWaves * MOE_GEMV_NS, a, cus)), dim3(256), lds, s, a);
+static hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
+  const int per = kGemmWaves * MOE_GEMV_NS;
+  constexpr int D = MOE_GEMV_D;
+  switch (scale_group(a.K / 128)) {
+    case 8: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 8 ? D : 8), 8>, per, a, kGemvRows, s);
+    case 4: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 4 ? D : 4), 4>, per, a, kGemvRows, s);
+    case 2: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 2 ? D : 2), 2>, per, a, kGemvRows, s);
+    default: return launch_one(k_gemm_gemv<MOE_GEMV_NS, 1, 1>, per, a, kGemvRows, s);
+  }
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
                                int a_rows, const int32_t* off, int E, const uint8_t* w, int N, int K,
                                float* out, int flags, int gemv_max_rows, hipStream_t s) {
-  int cus = 0;
-  hipError_t err = cu_count(&cus);
-  if (err != hipSuccess) return err;
-  const size_t lds = sizeof(uint16_t) * (size_t)E;
   const int big = 0x7FFFFFFF;
   // which groups each kernel owns
   int gemv_lo = 1, gemv_hi = 0, mfma_lo = 1;
@@ -423,22 +481,12 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
   }
   if (gemv_hi >= gemv_lo) {
     const GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, gemv_lo, gemv_hi};
-    switch (ring_depth(K, MOE_GEMV_D)) {
-      case 1: launch_gemv_d<1>(a, cus, lds, s); break;
-      case 2: launch_gemv_d<2>(a, cus, lds, s); break;
-      default: launch_gemv_d<(MOE_GEMV_D >= 4 ? 4 : MOE_GEMV_D)>(a, cus, lds, s); break;
-    }
-    err = hipGetLastError();
+    const hipError_t err = launch_gemv(a, s);
     if (err != hipSuccess) return err;
   }
   if (mfma_lo < big) {
     const GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, mfma_lo < 1 ? 1 : mfma_lo, big};
-    switch (ring_depth(K, MOE_GEMM_D)) {
-      case 1: launch_mfma_d<1>(a, cus, lds, s); break;
-      case 2: launch_mfma_d<2>(a, cus, lds, s); break;
-      default: launch_mfma_d<(MOE_GEMM_D >= 4 ? 4 : MOE_GEMM_D)>(a, cus, lds, s); break;
-    }
-    err = hipGetLastError();
+    const hipError_t err = launch_mfma(a, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -19,20 +19,41 @@ GEMM_TOL = 2e-3
 
 
 # ------------------------------------------------------------------------------ packing
+def _sign_folded(nib, scl):
+    """The canonical bytes nvfp4_unpack_weights documents for packed weights: every block
+    scale with its sign bit cleared and, in those blocks, the e2m1 sign bits flipped."""
+    neg = (scl & 0x80) != 0                                  # [rows, K/16]
+    flip = np.repeat(neg, 8, axis=1).astype(np.uint8) * 0x88  # 8 bytes per 16-block
+    return nib ^ flip, scl & 0x7F
+
+
+def _values(nib, scl):
+    v = onv.dequantize(nib, scl)
+    return np.where(np.isnan(v), 1e30, v)  # NaN scales compare equal to each other
+
+
 def test_pack_unpack_roundtrip_and_fused_concat(lib):
     import torch
     from nvfp4_block_scaled_gather_amd import binding as B
     rng = np.random.default_rng(1)
     for (E, N, K) in [(3, 48, 384), (2, 32, 4096), (1, 16, 128)]:
-        say("pack", E, N, K)
-        nib, scl = rand_nvfp4(rng, E * N, K, 0, 255)
-        wp = pack(B, nib, scl, E, N, K)
-        assert wp.numel() == E * N * K * 9 // 16
-        nib2 = empty((E * N, K // 2), torch.uint8)
-        scl2 = empty((E * N, K // 16), torch.uint8)
-        B.nvfp4_unpack_weights(wp, E, N, K, nib2, scl2)
-        sync()
-        assert np.array_equal(host(nib2), nib) and np.array_equal(host(scl2), scl)
+        for lo, hi in ((0, 0x7E), (0, 255)):
+            say("pack", E, N, K, "scales", lo, hi)
+            nib, scl = rand_nvfp4(rng, E * N, K, lo, hi)
+            wp = pack(B, nib, scl, E, N, K)
+            assert wp.numel() == E * N * K * 9 // 16
+            nib2 = empty((E * N, K // 2), torch.uint8)
+            scl2 = empty((E * N, K // 16), torch.uint8)
+            B.nvfp4_unpack_weights(wp, E, N, K, nib2, scl2)
+            sync()
+            n2, s2 = host(nib2), host(scl2)
+            fn, fs = _sign_folded(nib, scl)
+            assert np.array_equal(n2, fn) and np.array_equal(s2, fs)
+            if hi <= 0x7E:  # non-negative scales: an exact byte round trip
+                assert np.array_equal(n2, nib) and np.array_equal(s2, scl)
+            # the values (e2m1 x e4m3, signed zeros included) never change
+            v0, v1 = _values(nib, scl), _values(n2, s2)
+            assert np.array_equal(v0, v1) and np.array_equal(np.signbit(v0), np.signbit(v1))
     # fused gate|up packs to the concatenation of the separately packed halves
     I, K = 32, 256
     g, gs = rand_nvfp4(rng, I, K, 0, 255)

@@ -45,7 +45,7 @@ def parse():
                    help="second workload timed in the same run ('' for none)")
     p.add_argument("--flags", type=int, default=None, help="GEMM path (0 auto, 1 GEMV, 2 MFMA)")
     p.add_argument("--gemv-max-rows", type=int, default=None)
-    p.add_argument("--kernel-iters", type=int, default=20)
+    p.add_argument("--kernel-iters", type=int, default=30)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-experts", type=int, default=144,
                    help="experts in the oracle's bounded sample")
@@ -134,7 +134,7 @@ def time_w13(dl, iters):
         B.nvfp4_quantize_rows(xg, R, H, xq, xs, xgs)
         acc = e((R, 2 * I), torch.float32)
         flags, gmax = dl.desc.flags, dl.desc.gemv_max_rows
-        for _ in range(3):
+        for _ in range(10):  # to a steady clock after the layer runs
             B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gmax)
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)

@@ -140,7 +140,7 @@ int nvfp4_quantize_rows(const uint16_t* in, int R, int K, uint8_t* q, uint8_t* s
   if (R > 0) REQUIRE(in && q && sc && row_gs, MOE_EINVAL, "quantize: null pointer");
   REQUIRE(aligned(in, 16) && aligned(q, 8) && aligned(row_gs, 4), MOE_EINVAL,
           "quantize: in must be 16-byte and q 8-byte aligned");
-  return hip_status(moe::launch_quantize(in, nullptr, R, K, q, sc, row_gs, stream), "quantize launch");
+  return hip_status(moe::launch_quantize(in, nullptr, nullptr, R, K, q, sc, row_gs, stream), "quantize launch");
 }
 
 int grouped_gemm_nvfp4(const uint8_t* aq, const uint8_t* as, const int32_t* expert_offsets, int E,
@@ -200,7 +200,7 @@ struct LayerWs {
   uint8_t* xq;
   uint8_t* xs;
   float* xgs;
-  float* acc;  // acc13 [R, 2I], later reused for y [R, H]
+  float* acc;  // acc13 [R, 2I] (or h [R, I] bf16), later reused for y [R, H]
   uint8_t* hq;
   uint8_t* hs;
   float* hgs;
@@ -283,14 +283,31 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
                                  w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, x, H, w.xq, w.xs,
                                  w.xgs, stream);
   if (e != hipSuccess) return hip_status(e, "layer: group+quantize launch");
-  if (R > 0) {
-    e = moe::launch_grouped_gemm(w.xq, w.xs, w.row_src, S, w.offsets, E, (const uint8_t*)L->w13_packed,
-                                 2 * I, H, w.acc, L->flags, L->gemv_max_rows, stream);
-    if (e != hipSuccess) return hip_status(e, "layer: w13 GEMM launch");
+  const bool all_mfma = L->flags == MOE_PATH_FORCE_MFMA ||
+                        (L->flags == MOE_PATH_AUTO && L->gemv_max_rows == 0);
+  if (all_mfma) {
+    // SwiGLU in the w13 GEMM's epilogue (h in bf16 instead of the fp32 gate|up products),
+    // then the NVFP4 quantization of h; the same bits as the unfused sequence below
+    uint16_t* h = (uint16_t*)w.acc;
+    if (R > 0) {
+      e = moe::launch_grouped_gemm_swiglu(w.xq, w.xs, w.row_src, S, w.offsets, E,
+                                          (const uint8_t*)L->w13_packed, I, H, L->g_gate, L->g_up,
+                                          w.xgs, w.row_src, h, stream);
+      if (e != hipSuccess) return hip_status(e, "layer: w13 GEMM + SwiGLU launch");
+    }
+    e = moe::launch_quantize(h, nullptr, w.offsets + E, R, I, w.hq, w.hs, w.hgs, stream);
+    if (e != hipSuccess) return hip_status(e, "layer: quantize launch");
+  } else {
+    if (R > 0) {
+      e = moe::launch_grouped_gemm(w.xq, w.xs, w.row_src, S, w.offsets, E,
+                                   (const uint8_t*)L->w13_packed, 2 * I, H, w.acc, L->flags,
+                                   L->gemv_max_rows, stream);
+      if (e != hipSuccess) return hip_status(e, "layer: w13 GEMM launch");
+    }
+    e = moe::launch_swiglu(w.acc, R, I, w.offsets, E, L->g_gate, L->g_up, w.xgs, w.row_src, nullptr,
+                           w.hq, w.hs, w.hgs, stream);
+    if (e != hipSuccess) return hip_status(e, "layer: swiglu+quantize launch");
   }
-  e = moe::launch_swiglu(w.acc, R, I, w.offsets, E, L->g_gate, L->g_up, w.xgs, w.row_src, nullptr,
-                         w.hq, w.hs, w.hgs, stream);
-  if (e != hipSuccess) return hip_status(e, "layer: swiglu+quantize launch");
   if (R > 0) {
     e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, R, w.offsets, E, (const uint8_t*)L->w2_packed, H,
                                  I, w.acc, L->flags, L->gemv_max_rows, stream);

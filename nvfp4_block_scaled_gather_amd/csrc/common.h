@@ -107,6 +107,16 @@ __device__ __forceinline__ void e2m1x8_to_f16(uint32_t w, f16x2 out[4]) {
   out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
 }
 
+// ------------------------------------------------------------------------------ SwiGLU
+// One SwiGLU output as bf16 bits: zg = cg * ag, zu = cu * au (cg, cu: the row's gate / up
+// coefficient, activation global times the expert's weight global), silu(zg) * zu.  Shared
+// by the SwiGLU kernel and the fused w13 epilogue so that both give the same bits.
+__device__ __forceinline__ uint32_t swiglu_bf16(float cg, float ag, float cu, float au) {
+  const float zg = cg * ag, zu = cu * au;
+  const float silu = zg / (1.0f + expf(-zg));
+  return f32_to_bf16_rne(silu * zu);
+}
+
 // ------------------------------------------------------------------ packed weight layout
 // A matrix [N, K] is stored as N/16 tiles of 16 rows, an expert as N/16 consecutive tiles,
 // with no padding (N * K * 9/16 bytes per expert).  A tile covers K/128 chunks of 128
@@ -226,8 +236,10 @@ hipError_t launch_group(const int32_t* a_expert, const int32_t* a_src, const int
                         int32_t* tok_rows, int32_t* err_word, hipStream_t s);
 hipError_t launch_gather(const uint16_t* x, int H, const int32_t* row_src, int R, uint16_t* xg,
                          hipStream_t s);
-hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, int R, int K, uint8_t* q,
-                           uint8_t* sc, float* row_gs, hipStream_t s);
+// Output row i quantizes input row row_map[i] (row_map == nullptr: row i); rows at or past
+// *row_limit (row_limit != nullptr) and rows mapped to a negative index are all-zero rows.
+hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, const int32_t* row_limit,
+                           int R, int K, uint8_t* q, uint8_t* sc, float* row_gs, hipStream_t s);
 // row_gs of grouped row i is row_gs[gs_map[i]] (gs_map == nullptr: row_gs[i]).
 hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* expert_offsets, int E,
                          const float* g_gate, const float* g_up, const float* row_gs,
@@ -238,6 +250,15 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
                                int a_rows, const int32_t* expert_offsets, int E, const uint8_t* w,
                                int N, int K, float* out, int flags, int gemv_max_rows,
                                hipStream_t s);
+// The w13 GEMM with SwiGLU applied in its epilogue (MFMA path for every group): the
+// fused [2I, K] gate|up weights give h [R, I] bf16 for the grouped rows, equal bit for bit
+// to launch_grouped_gemm followed by launch_swiglu.  Rows outside every group are not
+// written.
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
+                                      int a_rows, const int32_t* expert_offsets, int E,
+                                      const uint8_t* w13, int I, int K, const float* g_gate,
+                                      const float* g_up, const float* row_gs,
+                                      const int32_t* gs_map, uint16_t* h, hipStream_t s);
 // Grouping and NVFP4 quantization of the S source rows of x in one launch (independent
 // work: block 0 groups, the other blocks quantize four rows each).
 hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,

@@ -61,6 +61,13 @@ struct GemmArgs {
   int N, K;
   float* out;
   int gmin, gmax;  // this kernel's groups: gmin <= G <= gmax
+  // SwiGLU epilogue (w13 with N = 2I): h [rows, I] bf16 instead of out
+  const float* g_gate;
+  const float* g_up;
+  const float* row_gs;
+  const int32_t* gs_map;  // grouped row i uses row_gs[gs_map[i]]; nullptr: row_gs[i]
+  uint16_t* h;
+  int I;
 };
 
 // ------------------------------------------------------------------------- LDS layout
@@ -163,14 +170,14 @@ __device__ __forceinline__ uint32_t chunk_scales(const u32x4& g, int j) {
 }
 
 // ------------------------------------------------------------------------- weight ring
-// Streams NS tiles (buffer wr, tiles tstride bytes apart) over all of K in scale groups of
+// Streams NS tiles (buffer wr, tiles sstride bytes apart) over all of K in scale groups of
 // S chunks with a ring of D chunks (D <= S, both powers of two, S divides NC = K / 128).
 // consume(c, j, wn, sg) uses chunk c (chunk j of its group): wn[s] holds its nibbles for
 // tile s and sg[s] the group's scales.  Loads in the main loop are unconditional and
 // pinned right after the use of their slot, so every wait is a counted one and the
 // prefetch distance stays D chunks.
 template <int NS, int D, int S, class Consume>
-__device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC, int tstride,
+__device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC, int sstride,
                                                int vw, int vs, Consume consume) {
   u32x4 wn[D][NS];
   u32x4 cur[NS], nxt[NS];
@@ -179,12 +186,12 @@ __device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       wn[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(
-          wr, vw, s * tstride + g * S * kChunkBytes + j * 1024, MOE_W_CPOL);
+          wr, vw, s * sstride + g * S * kChunkBytes + j * 1024, MOE_W_CPOL);
   };
   auto load_scales = [&](int g, u32x4 (&sg)[NS]) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      sg[s] = load_scale_group<S>(wr, vs, s * tstride + g * S * kChunkBytes);
+      sg[s] = load_scale_group<S>(wr, vs, s * sstride + g * S * kChunkBytes);
   };
   const int NG = NC / S;
   load_scales(0, cur);
@@ -222,10 +229,15 @@ __device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC
 // against them.  Every wave of the workgroup calls this together (it synchronizes); a
 // wave with no tile in this item (nsv <= 0) loads nothing (empty buffer range) and stores
 // nothing.
-template <int NS, int D, int S>
+//
+// SWI (NS == 2): the two tiles are a gate tile and the up tile I/16 tiles after it, and
+// the epilogue writes h = SwiGLU(gate, up) as bf16 (cg, cu: the expert's gate / up
+// weight globals) instead of the fp32 products.
+template <int NS, int D, int S, bool SWI>
 __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0,
-                                          uint8_t* s_q, uint8_t* s_s) {
+                                          uint8_t* s_q, uint8_t* s_s, float ggate, float gup) {
+  static_assert(!SWI || NS == 2, "the SwiGLU epilogue pairs one gate and one up tile");
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, r = lane & 15;
   const int K = p.K, NC = K / 128;
@@ -233,10 +245,11 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   // loads out of the pass loop (it would hold a second copy of the ring in registers).
   asm volatile("" ::: "memory");
   const int tstride = NC * kChunkBytes;
+  const int sstride = SWI ? (p.I / 16) * tstride : tstride;
+  const int range = nsv <= 0 ? 0 : SWI ? sstride + tstride : nsv * tstride;
   // (readfirstlane: the clamp may be computed on the vector unit, and a descriptor the
   // compiler believes divergent turns every load into a loop over lanes)
-  const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(wt, __builtin_amdgcn_readfirstlane((nsv > 0 ? nsv : 0) * tstride));
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, __builtin_amdgcn_readfirstlane(range));
 
   stage_rows(p, arow0, nrows, s_q, s_s);
   __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
@@ -253,7 +266,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   // chunk past the end land in the row padding or the next region: never used).
   u32x4 an_next = *(const u32x4*)aq_l;
   uint32_t asc_next = *(const uint16_t*)as_l;
-  stream_weights<NS, D, S>(wr, NC, tstride, 16 * lane, S * 1024 + 2 * S * lane,
+  stream_weights<NS, D, S>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
                            [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
     const u32x4 an = an_next;
     const uint32_t asc = asc_next;
@@ -276,7 +289,18 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   });
 
   // lane l holds out row r x weight rows 4 kq .. 4 kq + 3 of each tile
-  if (r < nrows) {
+  if (SWI) {
+    if (r < nrows && nsv > 0) {
+      const int i = arow0 + r;
+      const float gs = p.row_gs[p.gs_map ? p.gs_map[i] : i];
+      const float cg = gs * ggate, cu = gs * gup;
+      uint32_t hb[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) hb[x] = swiglu_bf16(cg, acc[0][x], cu, acc[1][x]);
+      const u32x2 v = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+      *(u32x2*)(p.h + (size_t)i * p.I + col0 + 4 * kq) = v;
+    }
+  } else if (r < nrows) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       if (s < nsv)
@@ -299,7 +323,7 @@ __device__ __forceinline__ ItemLoop item_loop(const GemmArgs& p, int nact, int N
   return L;
 }
 
-template <int NS, int D, int S>
+template <int NS, int D, int S, bool SWI>
 __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_nact;
@@ -308,19 +332,30 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
   uint8_t* s_q = smem + act_list_bytes(p.E);
   uint8_t* s_s = s_q + kPassRows * q_stride(p.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const ItemLoop L = item_loop(p, nact, NS);
+  // SWI: a wave owns one gate tile (and the matching up tile)
+  ItemLoop L;
+  if (SWI) {
+    L.tiles = p.I / 16;
+    L.per_item = kGemmWaves;
+    L.items_per_e = (L.tiles + L.per_item - 1) / L.per_item;
+    L.total = nact * L.items_per_e;
+  } else {
+    L = item_loop(p, nact, NS);
+  }
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
   for (int it = blockIdx.x; it < L.total; it += gridDim.x) {  // uniform over the workgroup
     const int e = __builtin_amdgcn_readfirstlane(s_act[it / L.items_per_e]);
-    const int t0 = (it % L.items_per_e) * L.per_item + wave * NS;
-    const int nsv = min(NS, L.tiles - t0);
+    const int t0 = (it % L.items_per_e) * L.per_item + wave * (SWI ? 1 : NS);
+    const int nsv = SWI ? (t0 < L.tiles ? 2 : 0) : min(NS, L.tiles - t0);
     const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
     const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
     const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+    const float ggate = SWI ? p.g_gate[e] : 0.f, gup = SWI ? p.g_up[e] : 0.f;
     for (int b = 0; b < G; b += kPassRows) {
       __syncthreads();  // the previous pass is done with the staged rows
-      mfma_pass<NS, D, S>(p, wt, nsv, r0 + b, min(kPassRows, G - b), 16 * t0, s_q, s_s);
+      mfma_pass<NS, D, S, SWI>(p, wt, nsv, r0 + b, min(kPassRows, G - b), 16 * t0, s_q, s_s,
+                               ggate, gup);
     }
   }
 }
@@ -444,15 +479,19 @@ static hipError_t launch_one(Kern kern, int per_item, const GemmArgs& a, int row
 
 // The packed layout's scale group S fixes the kernel instance; the ring depth is the
 // configured one, capped at S.
-static hipError_t launch_mfma(const GemmArgs& a, hipStream_t s) {
-  const int per = kGemmWaves * MOE_GEMM_NS;
+template <int NS, bool SWI>
+static hipError_t launch_mfma_t(const GemmArgs& a, int per, hipStream_t s) {
   constexpr int D = MOE_GEMM_D;
   switch (scale_group(a.K / 128)) {
-    case 8: return launch_one(k_gemm_mfma<MOE_GEMM_NS, (D < 8 ? D : 8), 8>, per, a, kPassRows, s);
-    case 4: return launch_one(k_gemm_mfma<MOE_GEMM_NS, (D < 4 ? D : 4), 4>, per, a, kPassRows, s);
-    case 2: return launch_one(k_gemm_mfma<MOE_GEMM_NS, (D < 2 ? D : 2), 2>, per, a, kPassRows, s);
-    default: return launch_one(k_gemm_mfma<MOE_GEMM_NS, 1, 1>, per, a, kPassRows, s);
+    case 8: return launch_one(k_gemm_mfma<NS, (D < 8 ? D : 8), 8, SWI>, per, a, kPassRows, s);
+    case 4: return launch_one(k_gemm_mfma<NS, (D < 4 ? D : 4), 4, SWI>, per, a, kPassRows, s);
+    case 2: return launch_one(k_gemm_mfma<NS, (D < 2 ? D : 2), 2, SWI>, per, a, kPassRows, s);
+    default: return launch_one(k_gemm_mfma<NS, 1, 1, SWI>, per, a, kPassRows, s);
   }
+}
+
+static hipError_t launch_mfma(const GemmArgs& a, hipStream_t s) {
+  return launch_mfma_t<MOE_GEMM_NS, false>(a, kGemmWaves * MOE_GEMM_NS, s);
 }
 
 static hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
@@ -464,6 +503,17 @@ static hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
     case 2: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 2 ? D : 2), 2>, per, a, kGemvRows, s);
     default: return launch_one(k_gemm_gemv<MOE_GEMV_NS, 1, 1>, per, a, kGemvRows, s);
   }
+}
+
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
+                                      int a_rows, const int32_t* off, int E, const uint8_t* w13,
+                                      int I, int K, const float* g_gate, const float* g_up,
+                                      const float* row_gs, const int32_t* gs_map, uint16_t* h,
+                                      hipStream_t s) {
+  GemmArgs a{aq, as, amap, a_rows, off, E, w13, 2 * I, K, nullptr, 1, 0x7FFFFFFF,
+             g_gate, g_up, row_gs, gs_map, h, I};
+  // one gate tile per wave: (I/16)/4 items per expert, the grid of N = 2I with 8 per item
+  return launch_mfma_t<2, true>(a, 2 * kGemmWaves, s);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,

@@ -13,12 +13,14 @@ namespace moe {
 // a negative entry: an all-zero row).
 template <int BPT>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ in,
-                                                  const int32_t* __restrict__ row_map, int K,
+                                                  const int32_t* __restrict__ row_map,
+                                                  const int32_t* __restrict__ row_limit, int K,
                                                   uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
                                                   float* __restrict__ row_gs) {
   __shared__ float s_red[4];
   const int row = blockIdx.x;
-  const int src = row_map ? row_map[row] : row;
+  int src = row_map ? row_map[row] : row;
+  if (row_limit && row >= *row_limit) src = -1;
   const int NB = K / 16;
   float v[BPT][16];
 #pragma unroll
@@ -37,14 +39,16 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ i
                           sc + (size_t)row * NB, row_gs + row);
 }
 
-hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, int R, int K, uint8_t* q,
-                           uint8_t* sc, float* row_gs, hipStream_t s) {
+hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, const int32_t* row_limit,
+                           int R, int K, uint8_t* q, uint8_t* sc, float* row_gs, hipStream_t s) {
   if (R == 0) return hipSuccess;
   const int NB = K / 16, nt = row_threads(NB);
   if (NB <= 256)
-    hipLaunchKernelGGL(k_quantize<1>, dim3(R), dim3(nt), 0, s, in, row_map, K, q, sc, row_gs);
+    hipLaunchKernelGGL(k_quantize<1>, dim3(R), dim3(nt), 0, s, in, row_map, row_limit, K, q, sc,
+                       row_gs);
   else
-    hipLaunchKernelGGL(k_quantize<2>, dim3(R), dim3(nt), 0, s, in, row_map, K, q, sc, row_gs);
+    hipLaunchKernelGGL(k_quantize<2>, dim3(R), dim3(nt), 0, s, in, row_map, row_limit, K, q, sc,
+                       row_gs);
   return hipGetLastError();
 }
 
@@ -102,9 +106,7 @@ __global__ __launch_bounds__(256) void k_swiglu(const float* __restrict__ acc13,
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const float zg = cg * ag[c][x], zu = cu * au[c][x];
-        const float silu = zg / (1.0f + expf(-zg));
-        v[k][4 * c + x] = __uint_as_float(f32_to_bf16_rne(silu * zu) << 16);  // bf16 value
+        v[k][4 * c + x] = __uint_as_float(swiglu_bf16(cg, ag[c][x], cu, au[c][x]) << 16);
       }
     }
   }

@@ -3,7 +3,10 @@
 
 A step is one moe_layer_forward call over one synthetic batch: grouping, gather +
 quantize, w13 grouped GEMM, SwiGLU + re-quantize, w2 grouped GEMM, scatter-add — every
-step of the path, inputs and packed weights already resident in HBM.
+step of the path, inputs and packed weights already resident in HBM.  The step is timed
+both as eager launches and as one HIP-graph replay of the same launches (the pages'
+graph-launched layer); the graph time is the reported value, and the run checks that a
+replay gives the eager output bit for bit.
 
 Metric (the pages' own byte model, table "Bytes decide it before the kernel runs" of the
 2026-09-06 page): weight-stream GB/s = active experts x 14,155,776 B / layer time.
@@ -47,6 +50,9 @@ def parse():
     p.add_argument("--gemv-max-rows", type=int, default=None)
     p.add_argument("--kernel-iters", type=int, default=30)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time eager launches only (default: also a HIP-graph replay of the "
+                        "layer, which is the reported value)")
     p.add_argument("--cpu-experts", type=int, default=144,
                    help="experts in the oracle's bounded sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -112,6 +118,26 @@ def time_layer(dl, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     return float(np.median(per)), float(np.min(per)), float(np.max(per)), wall
+
+
+def time_graph(dl, steps, warmup):
+    """The same layer step as time_layer, launched as one HIP-graph replay (the pages'
+    graph-launched variant): every kernel of the layer runs on every replay."""
+    import torch
+    graph = dl.capture_graph()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    per = []
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    for _ in range(steps):
+        start.record()
+        graph.replay()
+        stop.record()
+        stop.synchronize()
+        per.append(start.elapsed_time(stop))
+    return float(np.median(per)), float(np.min(per)), float(np.max(per)), graph
 
 
 def time_w13(dl, iters):
@@ -206,18 +232,33 @@ def run_workload(name, args, weights=None):
                    L.pack_expert_weights(wl.w2, wl.E, wl.H, wl.I))
         log("packed in %.1f s" % (time.perf_counter() - t0))
     dl = L.DeviceLayer(wl, weights=weights, **kw)
-    med, lo, hi, wall = time_layer(dl, args.steps, args.warmup)
+    e_med, e_lo, e_hi, wall = time_layer(dl, args.steps, args.warmup)
     err = dl.device_error()
     if err:
         raise RuntimeError("device error word %d" % err)
+    eager_out = dl.forward().clone()
+    torch.cuda.synchronize()
+    launch = "eager"
+    med, lo, hi = e_med, e_lo, e_hi
+    if not args.no_graph:
+        med, lo, hi, graph = time_graph(dl, args.steps, args.warmup)
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(dl.out, eager_out):  # a replay must give the eager bits
+            raise RuntimeError("graph replay output differs from the eager layer output")
+        launch = "hip-graph replay"
     n_act = len(wl.active_experts())
     wbytes = n_act * LAYER_BYTES_PER_EXPERT
     w13_ms = time_w13(dl, args.kernel_iters)
     res = {
         "workload": name, "expert_rows": wl.R, "tokens": wl.T, "active_experts": n_act,
-        "layer_ms_median": med, "layer_ms_min": lo, "layer_ms_max": hi, "layer_ms_wall": wall,
+        "launch": launch,
+        "layer_ms_median": med, "layer_ms_min": lo, "layer_ms_max": hi,
+        "layer_ms_eager_median": e_med, "layer_ms_eager_min": e_lo, "layer_ms_eager_max": e_hi,
+        "layer_ms_eager_wall": wall,
         "weight_bytes": wbytes, "weight_GBps": wbytes / (med * 1e-3) / 1e9,
         "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "frac_of_hbm_peak_eager": wbytes / (e_med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "w13_gemm_ms": w13_ms,
         "w13_GBps": n_act * W13_BYTES_PER_EXPERT / (w13_ms * 1e-3) / 1e9,
         "gemm_path": {"flags": dl.desc.flags, "gemv_max_rows": dl.desc.gemv_max_rows},
@@ -273,8 +314,11 @@ def main():
                    "experts": wl.E, "hidden": H, "intermediate": I, "expert_rows": R,
                    "active_experts": res["active_experts"], "weight_bytes": res["weight_bytes"],
                    "parallelism": "single GPU"},
+        "launch": res["launch"],
         "layer_ms": ms, "layer_ms_min": res["layer_ms_min"], "layer_ms_max": res["layer_ms_max"],
         "frac_of_hbm_peak": res["frac_of_hbm_peak"],
+        "layer_ms_eager": res["layer_ms_eager_median"],
+        "frac_of_hbm_peak_eager": res["frac_of_hbm_peak_eager"],
         "w13_gemm_ms": res["w13_gemm_ms"], "w13_weight_GBps": res["w13_GBps"],
         "roofline": roofline, "cpu_baseline": cpu, "also": also,
         "host": platform.node(),

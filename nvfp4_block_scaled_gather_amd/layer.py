@@ -81,6 +81,24 @@ class DeviceLayer:
     def device_error(self):
         return B.moe_get_device_error(self.ws_view)
 
+    def capture_graph(self):
+        """A HIP graph of one forward() (five kernel launches, no memset nodes); replaying
+        it recomputes self.out from the resident inputs.  Warmed up eagerly on the capture
+        stream first."""
+        import torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                self.forward()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward()
+        torch.cuda.synchronize()
+        return graph
+
     def weight_stream_bytes(self):
         """Weight bytes one layer call streams: active experts x (w13 + w2) packed bytes,
         the byte model of the page's table "Bytes decide it before the kernel runs"."""

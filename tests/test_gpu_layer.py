@@ -196,3 +196,29 @@ def test_full_size_layer_sampled_tokens(lib, full_weights, name):
     frac, worst = _e2e_ok(got[tokens], want)
     say("%s: fraction within tolerance %.5f, worst %.4f x RMS" % (name, frac, worst))
     assert frac >= E2E_FRAC
+
+
+# ------------------------------------------------------------------------------ HIP graph
+def test_graph_replay_matches_eager(lib):
+    """A captured layer replays to the eager output bit for bit, replay after replay, with
+    eager work between replays (no memset nodes are recorded)."""
+    import torch
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    for name, dims in (("tiny", {}), ("ragged570", dict(E=32, H=512, I=256)),
+                       ("zipf512", dict(E=48, H=256, I=256))):
+        say("graph", name, dims)
+        wl = W.make_workload(name, **dims)
+        dl = L.DeviceLayer(wl)
+        want = dl.forward().clone()
+        sync()
+        graph = dl.capture_graph()
+        for rep in range(4):
+            dl.out.zero_()
+            graph.replay()
+            sync()
+            assert torch.equal(dl.out, want), (name, rep)
+            dl.forward()  # eager launches between replays
+            sync()
+            assert torch.equal(dl.out, want), (name, rep)
+        assert dl.device_error() == 0

@@ -200,7 +200,7 @@ struct LayerWs {
   uint8_t* xq;
   uint8_t* xs;
   float* xgs;
-  float* acc;  // acc13 [R, 2I] (or h [R, I] bf16), later reused for y [R, H]
+  float* acc;  // acc13 [R, 2I] (or h [R, I] bf16), later reused for the scatter terms [R, H]
   uint8_t* hq;
   uint8_t* hs;
   float* hgs;
@@ -308,13 +308,15 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
                            w.hq, w.hs, w.hgs, stream);
     if (e != hipSuccess) return hip_status(e, "layer: swiglu+quantize launch");
   }
+  // w2 GEMM writing each grouped row's scatter term (row_w * g_down * hgs * y), then a
+  // per-token sum over the token lists: the bits of moe_scatter_add on y
   if (R > 0) {
     e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, R, w.offsets, E, (const uint8_t*)L->w2_packed, H,
-                                 I, w.acc, L->flags, L->gemv_max_rows, stream);
+                                 I, w.acc, L->flags, L->gemv_max_rows, stream, w.row_w, L->g_down,
+                                 w.hgs);
     if (e != hipSuccess) return hip_status(e, "layer: w2 GEMM launch");
   }
-  e = moe::launch_scatter(w.acc, R, H, w.offsets, E, w.row_w, L->g_down, w.hgs, w.tok_off, w.tok_rows,
-                          T, out, stream);
+  e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
   return hip_status(e, "layer: scatter launch");
 }
 

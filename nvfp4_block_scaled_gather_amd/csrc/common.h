@@ -40,14 +40,19 @@ __device__ __forceinline__ uint32_t e4m3_encode_pos(float v) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// Nearest e2m1 code of a float, ties to even (code LSB 0), saturating at 6, sign kept.
-// Decision points are the midpoints of the grid {0, .5, 1, 1.5, 2, 3, 4, 6}; at a
-// midpoint the even code wins, which decides "<" versus "<=".
+// Nearest e2m1 code of a finite float, ties to even (code LSB 0), saturating at 6, sign
+// kept (grid {0, .5, 1, 1.5, 2, 3, 4, 6}).  Below 1 the grid is uniform with step 0.5, so
+// the code there is rint(2|q|) (exact doubling); from 1 on, the float32 significand is
+// rounded to one bit with round-half-even on the bit pattern (a carry moves into the
+// exponent), saturating at code 7.  The two regimes are combined without a select or a
+// branch: min(|q|, 1) feeds the first and max(|q|, 1) the second, and the two codes of 1
+// (2 each) overlap.
 __device__ __forceinline__ uint32_t e2m1_encode(float q) {
   const float a = __builtin_fabsf(q);
-  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
-  return c | ((__float_as_uint(q) >> 28) & 8u);
+  const uint32_t sub = (uint32_t)__builtin_rintf(2.0f * __builtin_fminf(a, 1.0f));  // 0..2
+  const uint32_t b = __float_as_uint(__builtin_fmaxf(a, 1.0f));
+  const uint32_t nrm = min(((b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22) - 252u, 7u);  // 2..7
+  return (sub + nrm - 2u) | ((__float_as_uint(q) >> 28) & 8u);
 }
 
 // bf16 <-> float
@@ -204,7 +209,26 @@ __device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], in
     const uint32_t sb = e4m3_encode_pos(sf);
     const float d = e4m3_to_f32(sb) * gs;
     uint32_t lo = 0, hi = 0;
-    if (d != 0.0f) {
+    if (d >= 0x1p-60f && d <= 0x1p60f) {
+      // x / d correctly rounded without a division per element: the reciprocal refined by
+      // one Newton step, then the quotient x * y corrected twice by its exact residual
+      // fma(-d, q, x) (Markstein's method; the same operations as the IEEE division
+      // sequence when no operand needs rescaling, which holds for d in this range and
+      // every x whose quotient can reach the first decision point 0.25).  The residual
+      // steps turn a zero quotient of -0 into +0, so the sign is taken from x (d > 0).
+      float y = __builtin_amdgcn_rcpf(d);
+      y = fmaf(fmaf(-d, y, 1.0f), y, y);
+      auto quot = [&](float x) {
+        float q = x * y;
+        q = fmaf(fmaf(-d, q, x), y, q);
+        q = fmaf(fmaf(-d, q, x), y, q);
+        return __builtin_copysignf(q, x);  // a zero quotient keeps x's sign, as x / d does
+      };
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo |= e2m1_encode(quot(v[k][e])) << (4 * e);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hi |= e2m1_encode(quot(v[k][8 + e])) << (4 * e);
+    } else if (d != 0.0f) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) lo |= e2m1_encode(v[k][e] / d) << (4 * e);
 #pragma unroll
@@ -246,10 +270,13 @@ hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* expert
                          const int32_t* gs_map, uint16_t* h, uint8_t* q, uint8_t* sc,
                          float* h_gs, hipStream_t s);
 // Activation row of grouped row i is amap[i] (amap == nullptr: row i) of a_rows rows.
+// With c_w: grouped row i of expert e is multiplied by the fp32 product
+// c_w[i] * c_g[e] * c_gs[i] (each term of the scatter-add).
 hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
                                int a_rows, const int32_t* expert_offsets, int E, const uint8_t* w,
                                int N, int K, float* out, int flags, int gemv_max_rows,
-                               hipStream_t s);
+                               hipStream_t s, const float* c_w = nullptr,
+                               const float* c_g = nullptr, const float* c_gs = nullptr);
 // The w13 GEMM with SwiGLU applied in its epilogue (MFMA path for every group): the
 // fused [2I, K] gate|up weights give h [R, I] bf16 for the grouped rows, equal bit for bit
 // to launch_grouped_gemm followed by launch_swiglu.  Rows outside every group are not
@@ -271,4 +298,8 @@ hipError_t launch_scatter(const float* y, int R, int H, const int32_t* expert_of
                           const float* row_w, const float* g_down, const float* row_gs,
                           const int32_t* tok_off, const int32_t* tok_rows, int T, uint16_t* out,
                           hipStream_t s);
+// out[t] = bf16(sum of rows yc[tok_rows[p]], p = tok_off[t] .. tok_off[t+1] - 1), in
+// launch_scatter's order, for terms already scaled (the scatter-ready GEMM output).
+hipError_t launch_token_sum(const float* yc, int R, int H, const int32_t* tok_off,
+                            const int32_t* tok_rows, int T, uint16_t* out, hipStream_t s);
 }  // namespace moe

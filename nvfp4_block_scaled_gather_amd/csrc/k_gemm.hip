@@ -26,6 +26,11 @@
 //    k-quarters are summed across lanes at the end in a fixed tree.
 // Both dequantize exactly (dequant8 in common.h) and accumulate in fp32 in an order that
 // depends only on (N, K) and the path, never on the other rows of the group.
+//
+// Outputs are written with non-temporal stores: measured on MI355X, write-back stores that
+// are later evicted from L2 in the middle of the weight stream cost 4-5% of a GEMM at
+// these sizes (one to two microseconds per MB written), streaming stores less than half
+// of that.
 #include "common.h"
 
 #ifndef MOE_GEMM_NS
@@ -68,6 +73,12 @@ struct GemmArgs {
   const int32_t* gs_map;  // grouped row i uses row_gs[gs_map[i]]; nullptr: row_gs[i]
   uint16_t* h;
   int I;
+  // Scatter-ready output (w2 of the layer; c_w != nullptr): grouped row i is multiplied by
+  // c_w[i] * c_g[e] * c_gs[i] (router weight, the expert's down global, the row's
+  // activation global), the term the scatter-add sums.
+  const float* c_w;
+  const float* c_g;
+  const float* c_gs;
 };
 
 // ------------------------------------------------------------------------- LDS layout
@@ -231,8 +242,9 @@ __device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC
 // nothing.
 //
 // SWI (NS == 2): the two tiles are a gate tile and the up tile I/16 tiles after it, and
-// the epilogue writes h = SwiGLU(gate, up) as bf16 (cg, cu: the expert's gate / up
-// weight globals) instead of the fp32 products.
+// the epilogue writes h = SwiGLU(gate, up) as bf16 (ggate, gup: the expert's gate / up
+// weight globals) instead of the fp32 products.  Otherwise, with p.c_w, ggate is the
+// expert's down global of the scatter-ready epilogue.
 template <int NS, int D, int S, bool SWI>
 __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0,
@@ -250,6 +262,13 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   // (readfirstlane: the clamp may be computed on the vector unit, and a descriptor the
   // compiler believes divergent turns every load into a loop over lanes)
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, __builtin_amdgcn_readfirstlane(range));
+  // scatter-ready epilogue: this lane's coefficient inputs, loaded now so the epilogue
+  // does not wait on them
+  float ow = 0.f, ogs = 0.f;
+  if (!SWI && p.c_w && r < nrows) {
+    ow = p.c_w[arow0 + r];
+    ogs = p.c_gs[arow0 + r];
+  }
 
   stage_rows(p, arow0, nrows, s_q, s_s);
   __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
@@ -298,13 +317,21 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
 #pragma unroll
       for (int x = 0; x < 4; ++x) hb[x] = swiglu_bf16(cg, acc[0][x], cu, acc[1][x]);
       const u32x2 v = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-      *(u32x2*)(p.h + (size_t)i * p.I + col0 + 4 * kq) = v;
+      __builtin_nontemporal_store(v, (u32x2*)(p.h + (size_t)i * p.I + col0 + 4 * kq));
     }
   } else if (r < nrows) {
+    const size_t orow = arow0 + r;
+    const float cf = ow * ggate * ogs;  // ggate: the expert's down global here
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      if (s < nsv)
-        *(f32x4*)(p.out + (size_t)(arow0 + r) * p.N + col0 + 16 * s + 4 * kq) = acc[s];
+      f32x4 v = acc[s];
+      if (p.c_w) {
+        v[0] = v[0] * cf;
+        v[1] = v[1] * cf;
+        v[2] = v[2] * cf;
+        v[3] = v[3] * cf;
+      }
+      if (s < nsv) __builtin_nontemporal_store(v, (f32x4*)(p.out + orow * p.N + col0 + 16 * s + 4 * kq));
     }
   }
 }
@@ -351,7 +378,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
     const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
     const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
     const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
-    const float ggate = SWI ? p.g_gate[e] : 0.f, gup = SWI ? p.g_up[e] : 0.f;
+    const float ggate = SWI ? p.g_gate[e] : p.c_w ? p.c_g[e] : 0.f;
+    const float gup = SWI ? p.g_up[e] : 0.f;
     for (int b = 0; b < G; b += kPassRows) {
       __syncthreads();  // the previous pass is done with the staged rows
       mfma_pass<NS, D, S, SWI>(p, wt, nsv, r0 + b, min(kPassRows, G - b), 16 * t0, s_q, s_s,
@@ -364,7 +392,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
 template <int NS, int D, int S>
 __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0,
-                                          uint8_t* s_q, uint8_t* s_s) {
+                                          uint8_t* s_q, uint8_t* s_s, float gdown) {
   constexpr int NR = kGemvRows;
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4;
@@ -419,14 +447,18 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
   });
 
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int a = 0; a < NR; ++a) {
+    if (a >= nrows) break;  // uniform
+    const size_t orow = arow0 + a;
+    float cf = 1.0f;
+    if (p.c_w) cf = p.c_w[arow0 + a] * gdown * p.c_gs[arow0 + a];  // scatter-ready output
 #pragma unroll
-    for (int a = 0; a < NR; ++a) {
+    for (int s = 0; s < NS; ++s) {
       float v = acc[s][a];
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
-      if (s < nsv && a < nrows && lane < 16)
-        p.out[(size_t)(arow0 + a) * p.N + col0 + 16 * s + lane] = v;
+      if (p.c_w) v = v * cf;
+      if (s < nsv && lane < 16) __builtin_nontemporal_store(v, p.out + orow * p.N + col0 + 16 * s + lane);
     }
   }
 }
@@ -450,9 +482,10 @@ __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
     const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
     const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
     const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+    const float gdown = p.c_w ? p.c_g[e] : 0.f;
     for (int b = 0; b < G; b += kGemvRows) {
       __syncthreads();
-      gemv_pass<NS, D, S>(p, wt, nsv, r0 + b, min(kGemvRows, G - b), 16 * t0, s_q, s_s);
+      gemv_pass<NS, D, S>(p, wt, nsv, r0 + b, min(kGemvRows, G - b), 16 * t0, s_q, s_s, gdown);
     }
   }
 }
@@ -518,7 +551,8 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, cons
 
 hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
                                int a_rows, const int32_t* off, int E, const uint8_t* w, int N, int K,
-                               float* out, int flags, int gemv_max_rows, hipStream_t s) {
+                               float* out, int flags, int gemv_max_rows, hipStream_t s,
+                               const float* c_w, const float* c_g, const float* c_gs) {
   const int big = 0x7FFFFFFF;
   // which groups each kernel owns
   int gemv_lo = 1, gemv_hi = 0, mfma_lo = 1;
@@ -530,12 +564,18 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
     mfma_lo = gemv_max_rows + 1;
   }
   if (gemv_hi >= gemv_lo) {
-    const GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, gemv_lo, gemv_hi};
+    GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, gemv_lo, gemv_hi};
+    a.c_w = c_w;
+    a.c_g = c_g;
+    a.c_gs = c_gs;
     const hipError_t err = launch_gemv(a, s);
     if (err != hipSuccess) return err;
   }
   if (mfma_lo < big) {
-    const GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, mfma_lo < 1 ? 1 : mfma_lo, big};
+    GemmArgs a{aq, as, amap, a_rows, off, E, w, N, K, out, mfma_lo < 1 ? 1 : mfma_lo, big};
+    a.c_w = c_w;
+    a.c_g = c_g;
+    a.c_gs = c_gs;
     const hipError_t err = launch_mfma(a, s);
     if (err != hipSuccess) return err;
   }

@@ -112,13 +112,19 @@ __device__ void stable_place(int n, int nkeys, int* bucket_start, int* hist, int
   __syncthreads();
 }
 
-// LDS ints the grouping needs: the two histograms, plus the per-wave ones when parallel.
-__host__ __device__ inline size_t group_lds_ints(int E, int T, bool parallel) {
+// LDS ints the grouping needs: the two histograms, plus the per-wave ones when parallel,
+// plus (cached) the R assignments and the grouped rows' output rows.
+constexpr int kCachedInts = 5;  // per assignment: key, src, dst, weight; grouped dst
+__host__ __device__ inline size_t group_lds_ints(int E, int T, bool parallel, int R, bool cached) {
   const size_t base = (size_t)(E + 1) + (size_t)(T + 1);
-  return parallel ? base + (size_t)kGroupWaves * (size_t)((E > T ? E : T) + 1) : base;
+  const size_t par = parallel ? (size_t)kGroupWaves * (size_t)((E > T ? E : T) + 1) : 0;
+  return base + par + (cached ? (size_t)kCachedInts * (size_t)R : 0);
 }
 
-// The whole grouping, by one workgroup of kGroupThreads threads.
+// The whole grouping, by one workgroup of kGroupThreads threads.  CACHED: the assignments
+// are read from global memory once, into LDS, and every later phase reads LDS (the phases
+// are otherwise a chain of dependent global round trips).
+template <bool CACHED>
 __device__ void group_body(const int32_t* __restrict__ a_expert, const int32_t* __restrict__ a_src,
                            const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R,
                            int E, int S, int T, int32_t* __restrict__ expert_offsets,
@@ -129,6 +135,11 @@ __device__ void group_body(const int32_t* __restrict__ a_expert, const int32_t* 
   int* cnt_e = lds;                     // E + 1 (bucket E = dropped assignments)
   int* cnt_t = lds + (E + 1);           // T + 1
   int* hist = lds + (E + 1) + (T + 1);  // kGroupWaves x (max(E, T) + 1) when parallel
+  int* c_key = hist + (parallel ? kGroupWaves * ((E > T ? E : T) + 1) : 0);  // CACHED: R each
+  int* c_src = c_key + R;
+  int* c_dst = c_src + R;
+  float* c_w = (float*)(c_dst + R);
+  int* g_dst = c_dst + 2 * R;  // output row of grouped row i
   __shared__ int s_part[kGroupWaves];
   __shared__ int s_err;
   const int tid = threadIdx.x;
@@ -137,17 +148,42 @@ __device__ void group_body(const int32_t* __restrict__ a_expert, const int32_t* 
   for (int k = tid; k < T + 1; k += kGroupThreads) cnt_t[k] = 0;
   if (tid == 0) s_err = 0;
   __syncthreads();
-  // 1. validate and count
+  // 1. validate and count (four assignments' loads in flight per thread)
   int err = 0;
-  for (int j = tid; j < R; j += kGroupThreads) {
-    const int e = a_expert[j], s = a_src[j], d = a_dst[j];
-    int bad = 0;
-    if (e < 0 || e >= E) bad |= MOE_ERR_EXPERT;
-    if (s < 0 || s >= S) bad |= MOE_ERR_SRC;
-    if (d < 0 || d >= T) bad |= MOE_ERR_DST;
-    err |= bad;
-    atomicAdd(&cnt_e[bad ? E : e], 1);
-    if (!bad) atomicAdd(&cnt_t[d], 1);
+  for (int base = 0; base < R; base += 4 * kGroupThreads) {
+    int ev[4], sv[4], dv[4];
+    float wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = base + u * kGroupThreads + tid;
+      ev[u] = sv[u] = dv[u] = 0;
+      wv[u] = 0.f;
+      if (j < R) {
+        ev[u] = a_expert[j];
+        sv[u] = a_src[j];
+        dv[u] = a_dst[j];
+        if (CACHED) wv[u] = a_w[j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = base + u * kGroupThreads + tid;
+      if (j >= R) break;
+      const int e = ev[u], sr = sv[u], d = dv[u];
+      int bad = 0;
+      if (e < 0 || e >= E) bad |= MOE_ERR_EXPERT;
+      if (sr < 0 || sr >= S) bad |= MOE_ERR_SRC;
+      if (d < 0 || d >= T) bad |= MOE_ERR_DST;
+      err |= bad;
+      atomicAdd(&cnt_e[bad ? E : e], 1);
+      if (!bad) atomicAdd(&cnt_t[d], 1);
+      if (CACHED) {
+        c_key[j] = bad ? E : e;
+        c_src[j] = sr;
+        c_dst[j] = d;
+        c_w[j] = wv[u];
+      }
+    }
   }
   if (err) atomicOr(&s_err, err);
   __syncthreads();
@@ -160,20 +196,35 @@ __device__ void group_body(const int32_t* __restrict__ a_expert, const int32_t* 
   const int Rv = cnt_e[E];
   __syncthreads();
   // 3. grouped rows in (expert, assignment) order; dropped assignments last
-  auto key_e = [&](int j) -> int {
-    const int e = a_expert[j], s = a_src[j], d = a_dst[j];
-    const bool ok = e >= 0 && e < E && s >= 0 && s < S && d >= 0 && d < T;
-    return ok ? e : E;
-  };
-  stable_place(R, E + 1, cnt_e, hist, nw, key_e, [&](int j, int pos) {
-    const bool ok = pos < Rv;
-    row_src[pos] = ok ? a_src[j] : -1;
-    row_dst[pos] = ok ? a_dst[j] : -1;
-    row_w[pos] = ok ? a_w[j] : 0.f;
-  });
-  // 4. token lists, ascending grouped row (row_dst is visible after stable_place's barrier)
-  stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return row_dst[i]; },
-               [&](int i, int pos) { tok_rows[pos] = i; });
+  if constexpr (CACHED) {
+    stable_place(R, E + 1, cnt_e, hist, nw, [&](int j) -> int { return c_key[j]; },
+                 [&](int j, int pos) {
+                   const bool ok = pos < Rv;
+                   row_src[pos] = ok ? c_src[j] : -1;
+                   row_dst[pos] = ok ? c_dst[j] : -1;
+                   row_w[pos] = ok ? c_w[j] : 0.f;
+                   if (ok) g_dst[pos] = c_dst[j];
+                 });
+  } else {
+    auto key_e = [&](int j) -> int {
+      const int e = a_expert[j], sr = a_src[j], d = a_dst[j];
+      const bool ok = e >= 0 && e < E && sr >= 0 && sr < S && d >= 0 && d < T;
+      return ok ? e : E;
+    };
+    stable_place(R, E + 1, cnt_e, hist, nw, key_e, [&](int j, int pos) {
+      const bool ok = pos < Rv;
+      row_src[pos] = ok ? a_src[j] : -1;
+      row_dst[pos] = ok ? a_dst[j] : -1;
+      row_w[pos] = ok ? a_w[j] : 0.f;
+    });
+  }
+  // 4. token lists, ascending grouped row (the grouped rows' outputs are visible after
+  // stable_place's barrier)
+  auto place_tok = [&](int i, int pos) { tok_rows[pos] = i; };
+  if constexpr (CACHED)
+    stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return g_dst[i]; }, place_tok);
+  else
+    stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return row_dst[i]; }, place_tok);
 }
 
 __global__ __launch_bounds__(kGroupThreads) void k_group(
@@ -181,10 +232,14 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(
     const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R, int E, int S, int T,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
     float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
-    int32_t* __restrict__ err_word, bool parallel) {
+    int32_t* __restrict__ err_word, bool parallel, bool cached) {
   extern __shared__ int lds[];
-  group_body(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w,
-             tok_off, tok_rows, err_word, parallel, lds);
+  if (cached)
+    group_body<true>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
+                     row_w, tok_off, tok_rows, err_word, parallel, lds);
+  else
+    group_body<false>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
+                      row_w, tok_off, tok_rows, err_word, parallel, lds);
 }
 
 // Grouping (block 0) and NVFP4 quantization of the S source rows of x (the other blocks,
@@ -196,13 +251,18 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_quantize(
     const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R, int E, int S, int T,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
     float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
-    int32_t* __restrict__ err_word, bool parallel, const uint16_t* __restrict__ x, int H,
-    int nthreads, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs, float* __restrict__ xgs) {
+    int32_t* __restrict__ err_word, bool parallel, bool cached,
+    const uint16_t* __restrict__ x, int H, int nthreads, uint8_t* __restrict__ xq,
+    uint8_t* __restrict__ xs, float* __restrict__ xgs) {
   extern __shared__ int lds[];
   __shared__ float s_red[kGroupWaves];
   if (blockIdx.x == 0) {
-    group_body(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w,
-               tok_off, tok_rows, err_word, parallel, lds);
+    if (cached)
+      group_body<true>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
+                       row_w, tok_off, tok_rows, err_word, parallel, lds);
+    else
+      group_body<false>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
+                        row_w, tok_off, tok_rows, err_word, parallel, lds);
     return;
   }
   const int rows_per_block = kGroupThreads / nthreads;
@@ -229,18 +289,36 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_quantize(
                             xs + (size_t)row * NB, xgs + row);
 }
 
+// LDS of the grouping workgroup: per-wave histograms when they fit in 64 KiB; the cached
+// assignments on top when the total fits in the CU's 160 KiB.
+constexpr size_t kGroupLdsMax = 159 * 1024;  // the CU's 160 KiB less the static LDS
+
 static bool group_parallel(int E, int T) {
-  return group_lds_ints(E, T, true) * sizeof(int) <= 65536;
+  return group_lds_ints(E, T, true, 0, false) * sizeof(int) <= 65536;
+}
+
+static bool group_cached(int E, int T, int R) {
+  return group_lds_ints(E, T, group_parallel(E, T), R, true) * sizeof(int) <= kGroupLdsMax;
+}
+
+template <class Kern>
+static hipError_t set_lds(Kern kern, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
 }
 
 hipError_t launch_group(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
                         const float* a_w, int R, int E, int S, int T, int32_t* expert_offsets,
                         int32_t* row_src, int32_t* row_dst, float* row_w, int32_t* tok_off,
                         int32_t* tok_rows, int32_t* err_word, hipStream_t s) {
-  const bool par = group_parallel(E, T);
-  hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), group_lds_ints(E, T, par) * sizeof(int),
-                     s, a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
-                     row_w, tok_off, tok_rows, err_word, par);
+  const bool par = group_parallel(E, T), cached = group_cached(E, T, R);
+  const size_t lds = group_lds_ints(E, T, par, R, cached) * sizeof(int);
+  const hipError_t e = set_lds(k_group, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), lds, s, a_expert, a_src, a_dst, a_w, R,
+                     E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off, tok_rows, err_word,
+                     par, cached);
   return hipGetLastError();
 }
 
@@ -250,19 +328,24 @@ hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, 
                                  float* row_w, int32_t* tok_off, int32_t* tok_rows,
                                  int32_t* err_word, const uint16_t* x, int H, uint8_t* xq,
                                  uint8_t* xs, float* xgs, hipStream_t s) {
-  const bool par = group_parallel(E, T);
+  const bool par = group_parallel(E, T), cached = group_cached(E, T, R);
   const int NB = H / 16, nt = row_threads(NB);
   const int rows_per_block = kGroupThreads / nt;
   const dim3 grid(1 + (S + rows_per_block - 1) / rows_per_block);
-  const size_t lds = group_lds_ints(E, T, par) * sizeof(int);
-  if (NB <= 256)
+  const size_t lds = group_lds_ints(E, T, par, R, cached) * sizeof(int);
+  if (NB <= 256) {
+    const hipError_t e = set_lds(k_group_quantize<1>, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_group_quantize<1>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
                        a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
-                       tok_rows, err_word, par, x, H, nt, xq, xs, xgs);
-  else
+                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs);
+  } else {
+    const hipError_t e = set_lds(k_group_quantize<2>, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_group_quantize<2>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
                        a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
-                       tok_rows, err_word, par, x, H, nt, xq, xs, xgs);
+                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs);
+  }
   return hipGetLastError();
 }
 

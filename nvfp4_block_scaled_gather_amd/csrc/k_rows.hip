@@ -10,7 +10,9 @@ namespace moe {
 
 // ------------------------------------------------------------------------- quantize
 // One workgroup per output row i; its input is row row_map[i] (row_map == nullptr: row i;
-// a negative entry: an all-zero row).
+// a negative entry: an all-zero row); rows at or past *row_limit are all-zero rows.
+// Without a row map the row is loaded before the limit is known (it is in bounds either
+// way), so the two loads overlap.
 template <int BPT>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ in,
                                                   const int32_t* __restrict__ row_map,
@@ -19,8 +21,8 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ i
                                                   float* __restrict__ row_gs) {
   __shared__ float s_red[4];
   const int row = blockIdx.x;
-  int src = row_map ? row_map[row] : row;
-  if (row_limit && row >= *row_limit) src = -1;
+  const int src = row_map ? row_map[row] : row;
+  const bool live = !row_limit || row < *row_limit;
   const int NB = K / 16;
   float v[BPT][16];
 #pragma unroll
@@ -32,6 +34,7 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ i
       w0 = p[0];
       w1 = p[1];
     }
+    if (!live) w0 = w1 = u32x4{0u, 0u, 0u, 0u};
     bf16x16_to_f32(w0, w1, v[k]);
   }
   const float amax = row_amax_threads<BPT>(v, threadIdx.x, blockDim.x, s_red);
@@ -150,20 +153,24 @@ hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* offset
 }
 
 // ------------------------------------------------------------------------- scatter
-// Grid (T, ceil(H / 256)), 8 waves per workgroup, 4 columns per lane.  Wave w sums the
-// token's rows p = tok_off[t] + w, + 8, ... in ascending order, each scaled by
-// row_w * g_down * row_gs (the coefficients of up to 64 rows are computed by the lanes in
-// parallel); the eight partial rows are then added in wave order.  The summation order
-// depends only on the token's row count, so a token's output does not depend on the
-// other tokens of the batch.
-constexpr int kScatterWaves = 8;
+// Summation order of a token (both scatter kernels below, so the layer's fused path and
+// moe_scatter_add give the same bits): the token's rows p = tok_off[t] .. tok_off[t+1] - 1
+// are summed as 8 interleaved partial sums, partial j taking p - tok_off[t] = j, j + 8,
+// ... in ascending p, each term the fp32 product c_i * y[i] (c_i = row_w[i] * g_down[e] *
+// row_gs[i], rounded, no fused multiply-add); the partials are then added in order 0..7.
+// The order depends only on the token's own row count, so a token's output does not depend
+// on the other tokens of the batch.
+constexpr int kSumParts = 8;
 
-__global__ __launch_bounds__(64 * kScatterWaves) void k_scatter(
+// Grid (T, ceil(H / 256)), 8 waves per workgroup (wave w = partial w), 4 columns per lane;
+// the coefficients of up to 64 rows are computed by the lanes in parallel.
+__global__ __launch_bounds__(64 * kSumParts) void k_scatter(
     const float* __restrict__ y, int H, const int32_t* __restrict__ offsets, int E,
     const float* __restrict__ row_w, const float* __restrict__ g_down,
     const float* __restrict__ row_gs, const int32_t* __restrict__ tok_off,
     const int32_t* __restrict__ tok_rows, uint16_t* __restrict__ out) {
-  __shared__ f32x4 s_part[kScatterWaves][64];
+#pragma clang fp contract(off)
+  __shared__ f32x4 s_part[kSumParts][64];
   extern __shared__ int32_t s_off[];  // expert offsets, for the row -> expert searches
   for (int k = threadIdx.x; k <= E; k += blockDim.x) s_off[k] = offsets[k];
   __syncthreads();
@@ -172,9 +179,9 @@ __global__ __launch_bounds__(64 * kScatterWaves) void k_scatter(
   const bool cv = col < H;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int p0 = tok_off[t], p1 = tok_off[t + 1];
-  for (int base = p0 + wave; base < p1; base += 64 * kScatterWaves) {
+  for (int base = p0 + wave; base < p1; base += 64 * kSumParts) {
     // rows base + 8k, k < 64: coefficients in parallel
-    const int p = base + kScatterWaves * lane;
+    const int p = base + kSumParts * lane;
     int i = 0;
     float c = 0.0f;
     if (p < p1) {
@@ -182,17 +189,17 @@ __global__ __launch_bounds__(64 * kScatterWaves) void k_scatter(
       const int e = expert_of_row(s_off, E, i);
       c = (e < E) ? row_w[i] * g_down[e] * row_gs[i] : 0.0f;
     }
-    const int n = min(64, (p1 - base + kScatterWaves - 1) / kScatterWaves);
+    const int n = min(64, (p1 - base + kSumParts - 1) / kSumParts);
 #pragma unroll 4
     for (int k = 0; k < n; ++k) {
       const int ik = __shfl(i, k, 64);
       const float ck = __shfl(c, k, 64);
       if (cv) {
         const f32x4 yv = *(const f32x4*)(y + (size_t)ik * H + col);
-        acc[0] = fmaf(ck, yv[0], acc[0]);
-        acc[1] = fmaf(ck, yv[1], acc[1]);
-        acc[2] = fmaf(ck, yv[2], acc[2]);
-        acc[3] = fmaf(ck, yv[3], acc[3]);
+        acc[0] += ck * yv[0];
+        acc[1] += ck * yv[1];
+        acc[2] += ck * yv[2];
+        acc[3] += ck * yv[3];
       }
     }
   }
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(64 * kScatterWaves) void k_scatter(
   if (wave == 0 && cv) {
     f32x4 sum = s_part[0][lane];
 #pragma unroll
-    for (int w = 1; w < kScatterWaves; ++w) {
+    for (int w = 1; w < kSumParts; ++w) {
       const f32x4 o = s_part[w][lane];
       sum[0] += o[0];
       sum[1] += o[1];
@@ -221,9 +228,112 @@ hipError_t launch_scatter(const float* y, int R, int H, const int32_t* offsets, 
                           hipStream_t s) {
   (void)R;
   if (T == 0) return hipSuccess;
-  const dim3 grid(T, (H + 255) / 256), block(64 * kScatterWaves);
+  const dim3 grid(T, (H + 255) / 256), block(64 * kSumParts);
   hipLaunchKernelGGL(k_scatter, grid, block, sizeof(int32_t) * (size_t)(E + 1), s, y, H, offsets, E,
                      row_w, g_down, row_gs, tok_off, tok_rows, out);
+  return hipGetLastError();
+}
+
+// The layer's scatter once the terms are computed: yc[i] = c_i * y[i] for grouped row i
+// (written so by the w2 GEMM's epilogue, in grouped order: scattering them into token order
+// there measured slower than this gather), so token t sums rows yc[tok_rows[p]],
+// p = tok_off[t] .. tok_off[t+1] - 1, in the order above.
+// WIDE (tokens of many rows): the k_scatter shape, wave w = partial w, 4 columns per lane.
+// !WIDE (tokens of few rows): each wave owns 256 columns of the token and keeps the 8
+// partials in registers, four waves per workgroup over 1024 columns, so a workgroup is not
+// mostly idle waves and every lane has up to 8 independent loads in flight.
+template <bool WIDE>
+__global__ __launch_bounds__(256 * (WIDE ? 2 : 1)) void k_token_sum(
+    const float* __restrict__ yc, int H, const int32_t* __restrict__ tok_off,
+    const int32_t* __restrict__ tok_rows, uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p0 = tok_off[t], p1 = tok_off[t + 1];
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  int col;
+  if constexpr (WIDE) {
+    __shared__ f32x4 s_part[kSumParts][64];
+    col = blockIdx.y * 256 + 4 * lane;
+    const bool cv = col < H;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int base = p0 + wave; base < p1; base += 64 * kSumParts) {
+      // rows base + 8k, k < 64: their indices in parallel
+      const int p = base + kSumParts * lane;
+      const int i = p < p1 ? tok_rows[p] : 0;
+      const int n = min(64, (p1 - base + kSumParts - 1) / kSumParts);
+#pragma unroll 4
+      for (int k = 0; k < n; ++k) {
+        const int ik = __shfl(i, k, 64);
+        if (cv) {
+          const f32x4 v = *(const f32x4*)(yc + (size_t)ik * H + col);
+          acc[0] += v[0];
+          acc[1] += v[1];
+          acc[2] += v[2];
+          acc[3] += v[3];
+        }
+      }
+    }
+    s_part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0 || !cv) return;
+    sum = s_part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kSumParts; ++w) {
+      const f32x4 o = s_part[w][lane];
+      sum[0] += o[0];
+      sum[1] += o[1];
+      sum[2] += o[2];
+      sum[3] += o[3];
+    }
+  } else {
+    col = blockIdx.y * 1024 + wave * 256 + 4 * lane;
+    if (col >= H) return;  // no barrier in this shape
+    f32x4 part[kSumParts];
+#pragma unroll
+    for (int j = 0; j < kSumParts; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int base = p0; base < p1; base += kSumParts) {
+      int i[kSumParts];
+#pragma unroll
+      for (int j = 0; j < kSumParts; ++j) i[j] = base + j < p1 ? tok_rows[base + j] : 0;
+      f32x4 v[kSumParts];
+#pragma unroll
+      for (int j = 0; j < kSumParts; ++j)
+        if (base + j < p1) v[j] = *(const f32x4*)(yc + (size_t)i[j] * H + col);
+#pragma unroll
+      for (int j = 0; j < kSumParts; ++j) {
+        if (base + j < p1) {
+          part[j][0] += v[j][0];
+          part[j][1] += v[j][1];
+          part[j][2] += v[j][2];
+          part[j][3] += v[j][3];
+        }
+      }
+    }
+    sum = part[0];
+#pragma unroll
+    for (int j = 1; j < kSumParts; ++j) {
+      sum[0] += part[j][0];
+      sum[1] += part[j][1];
+      sum[2] += part[j][2];
+      sum[3] += part[j][3];
+    }
+  }
+  u32x2 ov;
+  ov[0] = f32_to_bf16_rne(sum[0]) | (f32_to_bf16_rne(sum[1]) << 16);
+  ov[1] = f32_to_bf16_rne(sum[2]) | (f32_to_bf16_rne(sum[3]) << 16);
+  *(u32x2*)(out + (size_t)t * H + col) = ov;
+}
+
+hipError_t launch_token_sum(const float* yc, int R, int H, const int32_t* tok_off,
+                            const int32_t* tok_rows, int T, uint16_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (R >= 16 * T) {  // many rows per token on average: split a token's rows over 8 waves
+    hipLaunchKernelGGL(k_token_sum<true>, dim3(T, (H + 255) / 256), dim3(64 * kSumParts), 0, s, yc,
+                       H, tok_off, tok_rows, out);
+  } else {
+    hipLaunchKernelGGL(k_token_sum<false>, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, yc, H,
+                       tok_off, tok_rows, out);
+  }
   return hipGetLastError();
 }
 

@@ -147,7 +147,7 @@ def _run_group(B, x, S, H, a_expert, a_src, a_dst, a_w, E, T):
 
 
 @pytest.mark.parametrize("case", ["random_invalid", "ragged570", "zipf", "empty", "one_expert",
-                                  "many_experts", "ragged2303"])
+                                  "many_experts", "ragged2303", "large_uncached"])
 def test_group_gather_bit_exact(lib, case):
     from nvfp4_block_scaled_gather_amd import binding as B
     say("group", case)
@@ -176,6 +176,11 @@ def test_group_gather_bit_exact(lib, case):
     elif case == "many_experts":      # key ranges too wide for per-wave histograms
         E, S, T, R = 3000, 700, 50, 700
         a_expert = rng.integers(-1, E + 1, R)
+        a_src = np.arange(R)
+        a_dst = rng.integers(0, T, R)
+    elif case == "large_uncached":    # too many assignments to hold in LDS: global reads
+        E, S, T, R = 64, 40000, 500, 40000
+        a_expert = rng.integers(-1, E, R)
         a_src = np.arange(R)
         a_dst = rng.integers(0, T, R)
     elif case == "ragged2303":

@@ -6,7 +6,10 @@ quantize, w13 grouped GEMM, SwiGLU + re-quantize, w2 grouped GEMM, scatter-add â
 step of the path, inputs and packed weights already resident in HBM.  The step is timed
 both as eager launches and as one HIP-graph replay of the same launches (the pages'
 graph-launched layer); the graph time is the reported value, and the run checks that a
-replay gives the eager output bit for bit.
+replay gives the eager output bit for bit.  Each timed block follows an untimed warm-up of
+at least --warmup steps and at least --settle-ms of continuous work (default 500 ms;
+measured on MI355X, the layer runs up to 10% slower during the first few hundred ms of
+work after the GPU was idle).
 
 Metric (the pages' own byte model, table "Bytes decide it before the kernel runs" of the
 2026-09-06 page): weight-stream GB/s = active experts x 14,155,776 B / layer time.
@@ -42,6 +45,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--settle-ms", type=float, default=500.0,
+                   help="the untimed warm-up before each timed block runs at least --warmup "
+                        "steps and at least this long (the GPU reaches steady clocks only "
+                        "after a few hundred ms of continuous work)")
     p.add_argument("--workload", default="ragged570",
                    choices=["ragged570", "ragged2303", "zipf512", "decode1"])
     p.add_argument("--also", default="ragged2303",
@@ -100,11 +107,23 @@ def measured_traffic(workload):
         return None
 
 
-def time_layer(dl, steps, warmup):
+def warm(step, warmup, settle_ms):
+    """Untimed warm-up: at least `warmup` steps and at least `settle_ms` of continuous work."""
     import torch
-    for _ in range(warmup):
-        dl.forward()
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < settle_ms:
+        step()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return n
+
+
+def time_layer(dl, steps, warmup, settle_ms=0.0):
+    import torch
+    warm(dl.forward, warmup, settle_ms)
     per = []
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -120,14 +139,12 @@ def time_layer(dl, steps, warmup):
     return float(np.median(per)), float(np.min(per)), float(np.max(per)), wall
 
 
-def time_graph(dl, steps, warmup):
+def time_graph(dl, steps, warmup, settle_ms=0.0):
     """The same layer step as time_layer, launched as one HIP-graph replay (the pages'
     graph-launched variant): every kernel of the layer runs on every replay."""
     import torch
     graph = dl.capture_graph()
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
+    warm(graph.replay, warmup, settle_ms)
     per = []
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -140,7 +157,7 @@ def time_graph(dl, steps, warmup):
     return float(np.median(per)), float(np.min(per)), float(np.max(per)), graph
 
 
-def time_w13(dl, iters):
+def time_w13(dl, iters, settle_ms=0.0):
     """Average duration of one w13 grouped-GEMM launch (grouped_gemm_nvfp4) on the layer's
     own quantized activations, HIP events on the launch stream."""
     import torch
@@ -160,8 +177,9 @@ def time_w13(dl, iters):
         B.nvfp4_quantize_rows(xg, R, H, xq, xs, xgs)
         acc = e((R, 2 * I), torch.float32)
         flags, gmax = dl.desc.flags, dl.desc.gemv_max_rows
-        for _ in range(10):  # to a steady clock after the layer runs
-            B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gmax)
+        # untimed: at least 10 launches and settle_ms of them, to steady clocks
+        warm(lambda: B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gmax),
+             10, settle_ms)
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         start.record(stream)
@@ -232,7 +250,7 @@ def run_workload(name, args, weights=None):
                    L.pack_expert_weights(wl.w2, wl.E, wl.H, wl.I))
         log("packed in %.1f s" % (time.perf_counter() - t0))
     dl = L.DeviceLayer(wl, weights=weights, **kw)
-    e_med, e_lo, e_hi, wall = time_layer(dl, args.steps, args.warmup)
+    e_med, e_lo, e_hi, wall = time_layer(dl, args.steps, args.warmup, args.settle_ms)
     err = dl.device_error()
     if err:
         raise RuntimeError("device error word %d" % err)
@@ -241,7 +259,7 @@ def run_workload(name, args, weights=None):
     launch = "eager"
     med, lo, hi = e_med, e_lo, e_hi
     if not args.no_graph:
-        med, lo, hi, graph = time_graph(dl, args.steps, args.warmup)
+        med, lo, hi, graph = time_graph(dl, args.steps, args.warmup, args.settle_ms)
         graph.replay()
         torch.cuda.synchronize()
         if not torch.equal(dl.out, eager_out):  # a replay must give the eager bits
@@ -249,7 +267,7 @@ def run_workload(name, args, weights=None):
         launch = "hip-graph replay"
     n_act = len(wl.active_experts())
     wbytes = n_act * LAYER_BYTES_PER_EXPERT
-    w13_ms = time_w13(dl, args.kernel_iters)
+    w13_ms = time_w13(dl, args.kernel_iters, args.settle_ms)
     res = {
         "workload": name, "expert_rows": wl.R, "tokens": wl.T, "active_experts": n_act,
         "launch": launch,
@@ -306,7 +324,7 @@ def main():
     ms = res["layer_ms_median"]
     line = {
         "metric": METRIC, "value": res["weight_GBps"], "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": args.steps, "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "nvfp4",
         "data": "synthetic",
         "config": {"workload": "%s: 288 experts, H=4096, I=2048, %d expert-rows, %d tokens"

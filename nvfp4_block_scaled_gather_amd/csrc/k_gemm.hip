@@ -27,10 +27,10 @@
 // Both dequantize exactly (dequant8 in common.h) and accumulate in fp32 in an order that
 // depends only on (N, K) and the path, never on the other rows of the group.
 //
-// Outputs are written with non-temporal stores: measured on MI355X, write-back stores that
-// are later evicted from L2 in the middle of the weight stream cost 4-5% of a GEMM at
-// these sizes (one to two microseconds per MB written), streaming stores less than half
-// of that.
+// Outputs are written with non-temporal stores of whole rows of the workgroup's block:
+// measured on MI355X, write-back stores that are later evicted from L2 in the middle of
+// the weight stream cost 4-5% of a GEMM at these sizes (one to two microseconds per MB
+// written), streaming stores less than half of that, and full-line stores less again.
 #include "common.h"
 
 #ifndef MOE_GEMM_NS
@@ -88,8 +88,12 @@ struct GemmArgs {
 __host__ __device__ __forceinline__ int act_list_bytes(int E) { return (2 * E + 15) & ~15; }
 __host__ __device__ __forceinline__ int q_stride(int K) { return K / 2 + 16; }
 __host__ __device__ __forceinline__ int s_stride(int K) { return K / 16 + 8; }
+// The staging area also holds the MFMA epilogue's output block (at most 16 rows x 132
+// floats), which for small K is larger than the staged rows.
+constexpr int kOutBlockBytes = kPassRows * 132 * 4;
 static size_t gemm_lds_bytes(int E, int K, int rows) {
-  return (size_t)act_list_bytes(E) + (size_t)rows * (q_stride(K) + s_stride(K));
+  const size_t stage = (size_t)rows * (q_stride(K) + s_stride(K));
+  return (size_t)act_list_bytes(E) + (stage > (size_t)kOutBlockBytes ? stage : (size_t)kOutBlockBytes);
 }
 
 // Ids of the experts whose group size is in [gmin, gmax], ascending, into LDS (wave 0).
@@ -307,8 +311,15 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     }
   });
 
-  // lane l holds out row r x weight rows 4 kq .. 4 kq + 3 of each tile
+  // Lane l holds out row r x weight rows 4 kq .. 4 kq + 3 of each tile.  The workgroup's
+  // output block (its rows x 128 columns, or x 64 h columns) is assembled in LDS over the
+  // staged rows and written as whole rows, so every store covers full 128-byte lines
+  // (written from the lanes directly, each line arrived in 32- or 64-byte pieces from
+  // four waves).
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // every wave is done with the staged rows: reuse them for the output
   if (SWI) {
+    uint16_t* so = (uint16_t*)s_q;  // [16][72] bf16 (within kOutBlockBytes)
     if (r < nrows && nsv > 0) {
       const int i = arow0 + r;
       const float gs = p.row_gs[p.gs_map ? p.gs_map[i] : i];
@@ -317,21 +328,41 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
 #pragma unroll
       for (int x = 0; x < 4; ++x) hb[x] = swiglu_bf16(cg, acc[0][x], cu, acc[1][x]);
       const u32x2 v = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-      __builtin_nontemporal_store(v, (u32x2*)(p.h + (size_t)i * p.I + col0 + 4 * kq));
+      *(u32x2*)(so + r * 72 + wave * 16 + 4 * kq) = v;
     }
-  } else if (r < nrows) {
-    const size_t orow = arow0 + r;
-    const float cf = ow * ggate * ogs;  // ggate: the expert's down global here
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      f32x4 v = acc[s];
-      if (p.c_w) {
-        v[0] = v[0] * cf;
-        v[1] = v[1] * cf;
-        v[2] = v[2] * cf;
-        v[3] = v[3] * cf;
+    __syncthreads();
+    const int colW = col0 - 16 * wave;
+    const int rr = lane >> 3, c = (lane & 7) * 8;
+    for (int row = rr + 8 * wave; row < nrows; row += 32) {
+      if (colW + c < p.I) {
+        const u32x4 v = *(const u32x4*)(so + row * 72 + c);
+        __builtin_nontemporal_store(v, (u32x4*)(p.h + (size_t)(arow0 + row) * p.I + colW + c));
       }
-      if (s < nsv) __builtin_nontemporal_store(v, (f32x4*)(p.out + orow * p.N + col0 + 16 * s + 4 * kq));
+    }
+  } else {
+    float* so = (float*)s_q;  // [16][132] floats (kOutBlockBytes)
+    if (r < nrows) {
+      const float cf = ow * ggate * ogs;  // ggate: the expert's down global here
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        f32x4 v = acc[s];
+        if (p.c_w) {
+          v[0] = v[0] * cf;
+          v[1] = v[1] * cf;
+          v[2] = v[2] * cf;
+          v[3] = v[3] * cf;
+        }
+        if (s < nsv) *(f32x4*)(so + r * 132 + wave * 32 + 16 * s + 4 * kq) = v;
+      }
+    }
+    __syncthreads();
+    const int colW = col0 - 32 * wave;
+    const int rr = lane >> 5, c = (lane & 31) * 4;
+    for (int row = rr + 2 * wave; row < nrows; row += 8) {
+      if (colW + c < p.N) {
+        const f32x4 v = *(const f32x4*)(so + row * 132 + c);
+        __builtin_nontemporal_store(v, (f32x4*)(p.out + (size_t)(arow0 + row) * p.N + colW + c));
+      }
     }
   }
 }

@@ -51,6 +51,11 @@ def parse():
                         "after a few hundred ms of continuous work)")
     p.add_argument("--workload", default="ragged570",
                    choices=["ragged570", "ragged2303", "zipf512", "decode1"])
+    p.add_argument("--no-decode-sweep", action="store_true",
+                   help="skip the decode-batch M sweep (M = 1 .. 32 token streams, top-8)")
+    p.add_argument("--flush-mb", type=int, default=512,
+                   help="device copy run before every timed decode-sweep call so that no "
+                        "expert weight is served from the 256 MB MALL or the L2s")
     p.add_argument("--also", default="ragged2303",
                    help="second workload timed in the same run ('' for none)")
     p.add_argument("--flags", type=int, default=None, help="GEMM path (0 auto, 1 GEMV, 2 MFMA)")
@@ -285,6 +290,59 @@ def run_workload(name, args, weights=None):
     return wl, dl, res, weights
 
 
+def decode_sweep(args, weights):
+    """The decode-batch M sweep ([GG] "Numbers", extended to M = 16 and 32): M token streams
+    with top-8 routing each, one layer call per step, on the full resident expert set.
+    Honest cache: before every timed call an untimed copy of --flush-mb MB (read and write)
+    replaces the MALL and L2 contents, so the active experts' weights come from HBM (their
+    113 MB at M=1 would otherwise fit in the 256 MB MALL).  Each call is a HIP-graph replay
+    (checked equal to the eager output) timed with HIP events; bytes per token are the
+    weight bytes streamed per step over M."""
+    import torch
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    nbytes = args.flush_mb << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out = []
+    for M in W.DECODE_SWEEP:
+        wl = W.make_workload("decode%d" % M)
+        dl = L.DeviceLayer(wl, weights=weights)
+        eager = dl.forward().clone()
+        graph = dl.capture_graph()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(dl.out, eager):
+            raise RuntimeError("decode%d: graph replay differs from the eager output" % M)
+
+        def step():
+            dst.copy_(src)
+            graph.replay()
+
+        warm(step, args.warmup, args.settle_ms)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            dst.copy_(src)
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        med = float(np.median(t))
+        n_act = len(wl.active_experts())
+        wbytes = n_act * LAYER_BYTES_PER_EXPERT
+        out.append({"M": M, "expert_rows": wl.R, "active_experts": n_act,
+                    "layer_us": med * 1e3, "layer_us_min": t[0] * 1e3,
+                    "weight_bytes": wbytes, "weight_GBps": wbytes / (med * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "weight_bytes_per_token": wbytes / M, "tokens_per_s": M / (med * 1e-3)})
+        log(json.dumps(out[-1]))
+        del graph, dl
+    return {"launch": "hip-graph replay, %d MB cache flush before each call" % args.flush_mb,
+            "points": out}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -306,6 +364,10 @@ def main():
         _, dl2, res2, _ = run_workload(args.also, args, weights)
         also[args.also] = res2
         del dl2
+    sweep = None
+    if not args.no_decode_sweep and wl.E == 288:
+        log("decode M sweep")
+        sweep = decode_sweep(args, weights)
 
     # dominant kernel: the w13 grouped GEMM (one grouped_gemm_nvfp4 call)
     R, H, I = wl.R, wl.H, wl.I
@@ -338,7 +400,7 @@ def main():
         "layer_ms_eager": res["layer_ms_eager_median"],
         "frac_of_hbm_peak_eager": res["frac_of_hbm_peak_eager"],
         "w13_gemm_ms": res["w13_gemm_ms"], "w13_weight_GBps": res["w13_GBps"],
-        "roofline": roofline, "cpu_baseline": cpu, "also": also,
+        "roofline": roofline, "cpu_baseline": cpu, "also": also, "decode_sweep": sweep,
         "host": platform.node(),
     }
     print(json.dumps(line), flush=True)

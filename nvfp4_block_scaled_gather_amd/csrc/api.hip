@@ -150,7 +150,7 @@ int grouped_gemm_nvfp4(const uint8_t* aq, const uint8_t* as, const int32_t* expe
   if (st != MOE_OK) return st;
   REQUIRE((long long)R * (K / 2) < (1ll << 31), MOE_EUNSUPPORTED,
           "grouped GEMM: activations of %d rows x %d columns exceed 2 GiB", R, K);
-  return hip_status(moe::launch_grouped_gemm(aq, as, nullptr, R, expert_offsets, E,
+  return hip_status(moe::launch_grouped_gemm(aq, as, nullptr, R, expert_offsets, E, R,
                                              (const uint8_t*)w_packed, N, K, out, flags,
                                              gemv_max_rows, stream),
                     "grouped GEMM launch");
@@ -290,7 +290,7 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
     // then the NVFP4 quantization of h; the same bits as the unfused sequence below
     uint16_t* h = (uint16_t*)w.acc;
     if (R > 0) {
-      e = moe::launch_grouped_gemm_swiglu(w.xq, w.xs, w.row_src, S, w.offsets, E,
+      e = moe::launch_grouped_gemm_swiglu(w.xq, w.xs, w.row_src, S, w.offsets, E, R,
                                           (const uint8_t*)L->w13_packed, I, H, L->g_gate, L->g_up,
                                           w.xgs, w.row_src, h, stream);
       if (e != hipSuccess) return hip_status(e, "layer: w13 GEMM + SwiGLU launch");
@@ -299,7 +299,7 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
     if (e != hipSuccess) return hip_status(e, "layer: quantize launch");
   } else {
     if (R > 0) {
-      e = moe::launch_grouped_gemm(w.xq, w.xs, w.row_src, S, w.offsets, E,
+      e = moe::launch_grouped_gemm(w.xq, w.xs, w.row_src, S, w.offsets, E, R,
                                    (const uint8_t*)L->w13_packed, 2 * I, H, w.acc, L->flags,
                                    L->gemv_max_rows, stream);
       if (e != hipSuccess) return hip_status(e, "layer: w13 GEMM launch");
@@ -311,9 +311,9 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
   // w2 GEMM writing each grouped row's scatter term (row_w * g_down * hgs * y), then a
   // per-token sum over the token lists: the bits of moe_scatter_add on y
   if (R > 0) {
-    e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, R, w.offsets, E, (const uint8_t*)L->w2_packed, H,
-                                 I, w.acc, L->flags, L->gemv_max_rows, stream, w.row_w, L->g_down,
-                                 w.hgs);
+    e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, R, w.offsets, E, R,
+                                 (const uint8_t*)L->w2_packed, H, I, w.acc, L->flags,
+                                 L->gemv_max_rows, stream, w.row_w, L->g_down, w.hgs);
     if (e != hipSuccess) return hip_status(e, "layer: w2 GEMM launch");
   }
   e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);

@@ -272,17 +272,18 @@ hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* expert
 // Activation row of grouped row i is amap[i] (amap == nullptr: row i) of a_rows rows.
 // With c_w: grouped row i of expert e is multiplied by the fp32 product
 // c_w[i] * c_g[e] * c_gs[i] (each term of the scatter-add).
+// R: the grouped rows (expert_offsets[E] <= R), which bounds the non-empty groups.
 hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
-                               int a_rows, const int32_t* expert_offsets, int E, const uint8_t* w,
-                               int N, int K, float* out, int flags, int gemv_max_rows,
-                               hipStream_t s, const float* c_w = nullptr,
+                               int a_rows, const int32_t* expert_offsets, int E, int R,
+                               const uint8_t* w, int N, int K, float* out, int flags,
+                               int gemv_max_rows, hipStream_t s, const float* c_w = nullptr,
                                const float* c_g = nullptr, const float* c_gs = nullptr);
 // The w13 GEMM with SwiGLU applied in its epilogue (MFMA path for every group): the
 // fused [2I, K] gate|up weights give h [R, I] bf16 for the grouped rows, equal bit for bit
 // to launch_grouped_gemm followed by launch_swiglu.  Rows outside every group are not
 // written.
 hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
-                                      int a_rows, const int32_t* expert_offsets, int E,
+                                      int a_rows, const int32_t* expert_offsets, int E, int R,
                                       const uint8_t* w13, int I, int K, const float* g_gate,
                                       const float* g_up, const float* row_gs,
                                       const int32_t* gs_map, uint16_t* h, hipStream_t s);

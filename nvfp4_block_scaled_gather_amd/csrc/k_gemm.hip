@@ -89,7 +89,8 @@ __host__ __device__ __forceinline__ int act_list_bytes(int E) { return (2 * E + 
 __host__ __device__ __forceinline__ int q_stride(int K) { return K / 2 + 16; }
 __host__ __device__ __forceinline__ int s_stride(int K) { return K / 16 + 8; }
 // The staging area also holds the MFMA epilogue's output block (at most 16 rows x 132
-// floats), which for small K is larger than the staged rows.
+// floats: 128 columns of two tiles per wave, plus padding), which for small K is larger
+// than the staged rows.
 constexpr int kOutBlockBytes = kPassRows * 132 * 4;
 static size_t gemm_lds_bytes(int E, int K, int rows) {
   const size_t stage = (size_t)rows * (q_stride(K) + s_stride(K));
@@ -254,6 +255,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
                                           int nsv, int arow0, int nrows, int col0,
                                           uint8_t* s_q, uint8_t* s_s, float ggate, float gup) {
   static_assert(!SWI || NS == 2, "the SwiGLU epilogue pairs one gate and one up tile");
+  static_assert(NS <= 2, "the output block in LDS holds two tiles per wave");
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, r = lane & 15;
   const int K = p.K, NC = K / 128;
@@ -340,7 +342,9 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
       }
     }
   } else {
-    float* so = (float*)s_q;  // [16][132] floats (kOutBlockBytes)
+    constexpr int WC = 16 * NS * kGemmWaves;  // the workgroup's output columns
+    constexpr int LPR = WC / 4, RPI = 64 / LPR;  // lanes per row, rows per store
+    float* so = (float*)s_q;  // [16][WC + 4] floats (within kOutBlockBytes)
     if (r < nrows) {
       const float cf = ow * ggate * ogs;  // ggate: the expert's down global here
 #pragma unroll
@@ -352,15 +356,15 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
           v[2] = v[2] * cf;
           v[3] = v[3] * cf;
         }
-        if (s < nsv) *(f32x4*)(so + r * 132 + wave * 32 + 16 * s + 4 * kq) = v;
+        if (s < nsv) *(f32x4*)(so + r * (WC + 4) + wave * 16 * NS + 16 * s + 4 * kq) = v;
       }
     }
     __syncthreads();
-    const int colW = col0 - 32 * wave;
-    const int rr = lane >> 5, c = (lane & 31) * 4;
-    for (int row = rr + 2 * wave; row < nrows; row += 8) {
+    const int colW = col0 - 16 * NS * wave;
+    const int rr = lane / LPR, c = (lane % LPR) * 4;
+    for (int row = rr + RPI * wave; row < nrows; row += RPI * kGemmWaves) {
       if (colW + c < p.N) {
-        const f32x4 v = *(const f32x4*)(so + row * 132 + c);
+        const f32x4 v = *(const f32x4*)(so + row * (WC + 4) + c);
         __builtin_nontemporal_store(v, (f32x4*)(p.out + (size_t)(arow0 + row) * p.N + colW + c));
       }
     }
@@ -522,68 +526,88 @@ __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------------- launch
-// One workgroup per possible item (workgroups past the active items exit after building
-// the active list).
-static int gemm_grid(int per_item, const GemmArgs& a) {
-  const long items_per_e = (a.N / 16 + per_item - 1) / per_item;
-  return (int)(items_per_e * a.E);
+// Grid: one workgroup per item that can have work.  At most min(E, R) groups are non-empty
+// (R grouped rows), so the grid is min(E, R) x items per expert; workgroups past the active
+// items exit after building the active list, and a workgroup loops over items if the grid
+// is smaller than their count.
+static int items_per_expert(int per_item, const GemmArgs& a) {
+  return (a.N / 16 + per_item - 1) / per_item;
 }
 
+static int gemm_grid(int per_item, const GemmArgs& a, int R) {
+  const long groups = R < a.E ? (R > 0 ? R : 1) : a.E;
+  return (int)(items_per_expert(per_item, a) * groups);
+}
+
+// A small batch (decode) fills few workgroups: at most this many items of 8 tiles.  Its
+// GEMMs then run the instance with a deeper weight ring (more bytes in flight per wave) and,
+// outside the SwiGLU epilogue, one tile per wave (twice the waves).  Both choices change
+// only which wave computes an output and how far ahead it loads, never the order of an
+// output's accumulation, so results do not depend on the batch.
+constexpr int kSmallGridItems = 2048;
+
 template <class Kern>
-static hipError_t launch_one(Kern kern, int per_item, const GemmArgs& a, int rows, hipStream_t s) {
+static hipError_t launch_one(Kern kern, int per_item, const GemmArgs& a, int rows, int R,
+                             hipStream_t s) {
   const size_t lds = gemm_lds_bytes(a.E, a.K, rows);
   if (lds > 65536) {
     const hipError_t err = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(gemm_grid(per_item, a)), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(gemm_grid(per_item, a, R)), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-// The packed layout's scale group S fixes the kernel instance; the ring depth is the
-// configured one, capped at S.
-template <int NS, bool SWI>
-static hipError_t launch_mfma_t(const GemmArgs& a, int per, hipStream_t s) {
-  constexpr int D = MOE_GEMM_D;
+// The packed layout's scale group S fixes the kernel instance; the ring depth D is capped
+// at S.
+template <int NS, int D, bool SWI>
+static hipError_t launch_mfma_t(const GemmArgs& a, int per, int R, hipStream_t s) {
   switch (scale_group(a.K / 128)) {
-    case 8: return launch_one(k_gemm_mfma<NS, (D < 8 ? D : 8), 8, SWI>, per, a, kPassRows, s);
-    case 4: return launch_one(k_gemm_mfma<NS, (D < 4 ? D : 4), 4, SWI>, per, a, kPassRows, s);
-    case 2: return launch_one(k_gemm_mfma<NS, (D < 2 ? D : 2), 2, SWI>, per, a, kPassRows, s);
-    default: return launch_one(k_gemm_mfma<NS, 1, 1, SWI>, per, a, kPassRows, s);
+    case 8: return launch_one(k_gemm_mfma<NS, (D < 8 ? D : 8), 8, SWI>, per, a, kPassRows, R, s);
+    case 4: return launch_one(k_gemm_mfma<NS, (D < 4 ? D : 4), 4, SWI>, per, a, kPassRows, R, s);
+    case 2: return launch_one(k_gemm_mfma<NS, (D < 2 ? D : 2), 2, SWI>, per, a, kPassRows, R, s);
+    default: return launch_one(k_gemm_mfma<NS, 1, 1, SWI>, per, a, kPassRows, R, s);
   }
 }
 
-static hipError_t launch_mfma(const GemmArgs& a, hipStream_t s) {
-  return launch_mfma_t<MOE_GEMM_NS, false>(a, kGemmWaves * MOE_GEMM_NS, s);
+static bool small_grid(const GemmArgs& a, int R) {
+  return gemm_grid(kGemmWaves * 2, a, R) <= kSmallGridItems;
 }
 
-static hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_mfma(const GemmArgs& a, int R, hipStream_t s) {
+  if (small_grid(a, R)) return launch_mfma_t<1, 8, false>(a, kGemmWaves, R, s);
+  return launch_mfma_t<MOE_GEMM_NS, MOE_GEMM_D, false>(a, kGemmWaves * MOE_GEMM_NS, R, s);
+}
+
+static hipError_t launch_gemv(const GemmArgs& a, int R, hipStream_t s) {
   const int per = kGemmWaves * MOE_GEMV_NS;
   constexpr int D = MOE_GEMV_D;
   switch (scale_group(a.K / 128)) {
-    case 8: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 8 ? D : 8), 8>, per, a, kGemvRows, s);
-    case 4: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 4 ? D : 4), 4>, per, a, kGemvRows, s);
-    case 2: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 2 ? D : 2), 2>, per, a, kGemvRows, s);
-    default: return launch_one(k_gemm_gemv<MOE_GEMV_NS, 1, 1>, per, a, kGemvRows, s);
+    case 8: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 8 ? D : 8), 8>, per, a, kGemvRows, R, s);
+    case 4: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 4 ? D : 4), 4>, per, a, kGemvRows, R, s);
+    case 2: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 2 ? D : 2), 2>, per, a, kGemvRows, R, s);
+    default: return launch_one(k_gemm_gemv<MOE_GEMV_NS, 1, 1>, per, a, kGemvRows, R, s);
   }
 }
 
 hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
-                                      int a_rows, const int32_t* off, int E, const uint8_t* w13,
-                                      int I, int K, const float* g_gate, const float* g_up,
-                                      const float* row_gs, const int32_t* gs_map, uint16_t* h,
-                                      hipStream_t s) {
+                                      int a_rows, const int32_t* off, int E, int R,
+                                      const uint8_t* w13, int I, int K, const float* g_gate,
+                                      const float* g_up, const float* row_gs,
+                                      const int32_t* gs_map, uint16_t* h, hipStream_t s) {
   GemmArgs a{aq, as, amap, a_rows, off, E, w13, 2 * I, K, nullptr, 1, 0x7FFFFFFF,
              g_gate, g_up, row_gs, gs_map, h, I};
   // one gate tile per wave: (I/16)/4 items per expert, the grid of N = 2I with 8 per item
-  return launch_mfma_t<2, true>(a, 2 * kGemmWaves, s);
+  if (small_grid(a, R)) return launch_mfma_t<2, 8, true>(a, 2 * kGemmWaves, R, s);
+  return launch_mfma_t<2, MOE_GEMM_D, true>(a, 2 * kGemmWaves, R, s);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
-                               int a_rows, const int32_t* off, int E, const uint8_t* w, int N, int K,
-                               float* out, int flags, int gemv_max_rows, hipStream_t s,
-                               const float* c_w, const float* c_g, const float* c_gs) {
+                               int a_rows, const int32_t* off, int E, int R, const uint8_t* w,
+                               int N, int K, float* out, int flags, int gemv_max_rows,
+                               hipStream_t s, const float* c_w, const float* c_g,
+                               const float* c_gs) {
   const int big = 0x7FFFFFFF;
   // which groups each kernel owns
   int gemv_lo = 1, gemv_hi = 0, mfma_lo = 1;
@@ -599,7 +623,7 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
     a.c_w = c_w;
     a.c_g = c_g;
     a.c_gs = c_gs;
-    const hipError_t err = launch_gemv(a, s);
+    const hipError_t err = launch_gemv(a, R, s);
     if (err != hipSuccess) return err;
   }
   if (mfma_lo < big) {
@@ -607,7 +631,7 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
     a.c_w = c_w;
     a.c_g = c_g;
     a.c_gs = c_gs;
-    const hipError_t err = launch_mfma(a, s);
+    const hipError_t err = launch_mfma(a, R, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -13,6 +13,9 @@ and real prompts that are not available; these stand in for them):
   ([MF] "Layer time" / "Tiles below M=8": ragged per-expert M, 570 tokens).
 * ``ragged2303``: 288 experts, 2303 expert-rows, 288 output rows of 8 (7 for the last).
 * ``zipf512``: 64 tokens, top-8 over 288 experts with Zipf(1.1) popularity.
+* ``decode2`` .. ``decode32``: the decode-batch M sweep ([GG] "Numbers", extended past M=8
+  as its "Next" list asks): M = 2, 4, 8, 16, 32 token streams, each top-8 over N(0,1)
+  logits, as decode1.
 
 Weights for expert e and tensor t come from a counter-based Philox stream keyed by
 (weight_seed, e, t), so any expert can be regenerated alone.  The four full-size workloads
@@ -30,7 +33,9 @@ G_DOWN = np.float32(4.2e-5)
 TENSOR_W13 = 0
 TENSOR_W2 = 1
 
-WORKLOADS = ("tiny", "decode1", "ragged570", "ragged2303", "zipf512")
+WORKLOADS = ("tiny", "decode1", "ragged570", "ragged2303", "zipf512",
+             "decode2", "decode4", "decode8", "decode16", "decode32")
+DECODE_SWEEP = (1, 2, 4, 8, 16, 32)  # token streams of the decode M-sweep
 BASE_SEED = 20260906
 
 
@@ -149,8 +154,8 @@ def make_workload(name, seed=None, E=None, H=None, I=None, weight_seed=None):
         T = 4
         a_expert, a_src, a_dst, a_w = _topk_workload(name, seed, E, H, I, T, 2)
         S = T
-    elif name == "decode1":
-        T = 1
+    elif name.startswith("decode"):
+        T = int(name[len("decode"):])
         a_expert, a_src, a_dst, a_w = _topk_workload(name, seed, E, H, I, T, min(8, E))
         S = T
     elif name in ("ragged570", "ragged2303"):

@@ -331,6 +331,30 @@ def test_gemm_row_invariance_within_path(lib, flags, sizes):
         assert np.array_equal(grouped.view(np.uint32), alone[:g].view(np.uint32)), g
 
 
+@pytest.mark.parametrize("flags", [0, 2])
+def test_gemm_grid_paths_agree_bitwise(lib, flags):
+    """A small batch (few non-empty groups: the deep-ring, one-tile-per-wave instance) and a
+    large one (the two-tiles-per-wave instance) give the same bits for the same rows: the
+    instance changes which wave computes an output, never its accumulation order."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm grid paths", flags)
+    rng = np.random.default_rng(80 + flags)
+    E, N, K = 600, 1024, 256
+    wn, wsc = rand_nvfp4(rng, E * N, K, 0x20, 0x40)
+    wp = pack(B, wn, wsc, E, N, K)
+    sizes = np.full(E, 2)
+    big_off = offsets_from_sizes(sizes)
+    aq, as_ = _workload_like(rng, int(big_off[-1]), K)
+    big = run_gemm(B, aq, as_, big_off, wp, N, K, flags, gemv_max=0)  # 600 groups: large grid
+    pick = [0, 299, 599]
+    rows = np.concatenate([np.arange(big_off[e], big_off[e + 1]) for e in pick])
+    small_sizes = np.zeros(E, np.int64)
+    small_sizes[pick] = 2
+    small_off = offsets_from_sizes(small_sizes)
+    small = run_gemm(B, aq[rows], as_[rows], small_off, wp, N, K, flags, gemv_max=0)  # 3 groups
+    assert np.array_equal(small.view(np.uint32), big[rows].view(np.uint32))
+
+
 @pytest.mark.parametrize("flags", [1, 2])
 def test_gemm_fused_w13_equals_separate_and_is_deterministic(lib, flags):
     """2026-09-07 page, section "Proof": fused gate|up == gate-only and up-only GEMMs,

@@ -127,6 +127,27 @@ def test_layer_batch_parity_and_determinism(lib, flags):
         assert not np.delete(alone, t, axis=0).any()
 
 
+def test_layer_batch_parity_across_grid_paths(lib):
+    """Batch parity where the full batch runs the large-grid GEMM instances (w13 with the
+    SwiGLU epilogue and w2, both above the small-grid threshold) and a single token the
+    small-grid ones: the token's output bits are the same."""
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("batch parity across grid paths")
+    wl = W.make_workload("zipf512", E=160, H=2048, I=1024)
+    dl = L.DeviceLayer(wl)
+    full = host(dl.forward()).copy()
+    assert dl.device_error() == 0
+    for t in (3, 40):
+        sel = np.where(wl.a_dst == t)[0]
+        one = W.Workload(**{**wl.__dict__, "a_expert": wl.a_expert[sel], "a_src": wl.a_src[sel],
+                            "a_dst": wl.a_dst[sel], "a_w": wl.a_w[sel]})
+        d1 = L.DeviceLayer(one, weights=(dl.w13, dl.w2))
+        alone = host(d1.forward())
+        sync()
+        assert np.array_equal(alone[t], full[t]), t
+
+
 def test_layer_drops_invalid_assignments(lib):
     """Out-of-range expert / source / output ids set the device error word and are
     dropped; the rest of the batch is computed as if they were absent."""
@@ -168,6 +189,8 @@ def _pick_tokens(wl, name):
     counts = np.bincount(wl.a_dst, minlength=wl.T)
     if name == "decode1":
         return [0]
+    if name.startswith("decode"):
+        return [0, wl.T - 1]
     if name == "ragged570":
         return [int(np.argmin(counts))]
     if name == "ragged2303":
@@ -177,7 +200,8 @@ def _pick_tokens(wl, name):
     return sorted({t_hot, 5})
 
 
-@pytest.mark.parametrize("name", ["decode1", "ragged570", "ragged2303", "zipf512"])
+@pytest.mark.parametrize("name", ["decode1", "ragged570", "ragged2303", "zipf512", "decode4",
+                                  "decode32"])
 def test_full_size_layer_sampled_tokens(lib, full_weights, name):
     """The full-size workloads in the launch configuration the benchmark times; the
     oracle recomputes a few whole output rows (every row of those tokens)."""

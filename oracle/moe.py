@@ -3,7 +3,10 @@
 The layer is the routed-expert loop of [GG] section "What changed":
   gather -> quantize -> grouped GEMM (w13, fused gate|up) -> SwiGLU (per-half globals)
   -> quantize -> grouped GEMM (w2) -> scatter-add weighted by router weight * down global.
-Each function below is one of those steps, in float64 unless stated otherwise.
+Each function below is one of those steps, in float64 unless stated otherwise.  The W4A16
+variant (grouped_gemm_w4a16, layer_forward_w4a16) is the same loop without the two
+activation quantizations: bf16 activations against the NVFP4 weights, the arithmetic of
+the pages' dequant-GEMV path ([GG] "Numbers").
 
 Notation: E experts, H hidden, I intermediate, S activation source rows, T output rows
 (tokens), R assignments ("expert-rows").  An assignment j routes source row a_src[j] to
@@ -118,6 +121,30 @@ def grouped_gemm(aq, as_, offsets, weights, N, K):
     return acc
 
 
+def grouped_gemm_w4a16(a_bits, offsets, weights, N, K):
+    """W4A16: acc[i, n] = sum_k x(i, k) * w_e(n, k) for every row i of expert e's group, in
+    float64, with x the row's bf16 values taken exactly (no activation quantization) and w
+    the exact NVFP4 weight values.  This is the arithmetic of the pages' dequant-GEMV loop
+    ([GG] "Numbers": exact BF16 activations against an NVFP4 weight).  ``a_bits``: bf16 bit
+    patterns [R, K]; rows outside every group are left at zero.
+    """
+    offsets = np.asarray(offsets)
+    E = len(offsets) - 1
+    a = nvfp4.bf16_bits_to_f32(np.asarray(a_bits, dtype=np.uint16)).astype(np.float64)
+    R = a.shape[0]
+    acc = np.zeros((R, N), dtype=np.float64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        w_nib, w_sc = weights(e)
+        assert w_nib.shape == (N, K // 2) and w_sc.shape == (N, K // 16)
+        wd = nvfp4.dequantize(w_nib, w_sc)
+        for i in range(r0, r1):
+            acc[i] = wd @ a[i]
+    return acc
+
+
 def silu(z):
     """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), float64."""
     with np.errstate(over="ignore"):
@@ -191,4 +218,26 @@ def layer_forward(x_bits, a_expert, a_src, a_dst, a_w, T, w13, w2, g_gate, g_up,
     if return_intermediates:
         return out, dict(group=g, Rv=Rv, xg=xg, xq=xq, xs=xs, xgs=xgs, acc13=acc13, h=h,
                          hq=hq, hs=hs, hgs=hgs, y=y)
+    return out
+
+
+def layer_forward_w4a16(x_bits, a_expert, a_src, a_dst, a_w, T, w13, w2, g_gate, g_up,
+                        g_down, E, H, I, return_intermediates=False):
+    """The routed-expert layer in W4A16 arithmetic (the same seven steps without the two
+    activation quantizations): gathered bf16 rows against the NVFP4 w13, SwiGLU with the
+    gate / up globals alone (no activation global: the activations carry none), bf16 h
+    against the NVFP4 w2, scatter-add weighted by router weight * down global.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    S = x_bits.shape[0]
+    g = group_rows(a_expert, a_src, a_dst, a_w, E, S, T)
+    R = len(g["row_src"])
+    ones = np.ones(R, dtype=np.float32)
+    xg = gather_rows(x_bits, g["row_src"])
+    acc13 = grouped_gemm_w4a16(xg, g["offsets"], w13, 2 * I, H)
+    h = swiglu(acc13, g["offsets"], g_gate, g_up, ones, I)
+    y = grouped_gemm_w4a16(h, g["offsets"], w2, H, I)
+    out = scatter_add(y, g["offsets"], g["row_w"], g_down, ones, g["tok_off"], g["tok_rows"], T)
+    if return_intermediates:
+        return out, dict(group=g, xg=xg, acc13=acc13, h=h, y=y)
     return out

@@ -251,3 +251,124 @@ def test_layer_output_scale_is_sane():
     d = _tiny_layer_inputs(22)
     out = nvfp4.bf16_bits_to_f32(_run(d))
     assert np.all(np.isfinite(out)) and np.abs(out).max() > 0
+
+
+# --------------------------------------------------------------------------- W4A16
+def _bf16_rows(rng, R, K, lo_exp=-1, hi_exp=1):
+    """bf16 bit patterns of random values +-(1 + m/128) * 2^e, e in [lo_exp, hi_exp]."""
+    m = rng.integers(0, 128, (R, K))
+    e = rng.integers(lo_exp, hi_exp + 1, (R, K))
+    sign = rng.integers(0, 2, (R, K))
+    return ((sign << 15) | ((e + 127) << 7) | m).astype(np.uint16)
+
+
+def _bf16_val(bits):
+    """Exact value of a bf16 bit pattern, decoded by hand (normal numbers)."""
+    b = int(bits)
+    e, m = (b >> 7) & 0xFF, b & 0x7F
+    v = (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127)
+    return -v if b & 0x8000 else v
+
+
+def test_w4a16_gemm_exact_against_rational_brute_force():
+    """K <= 256 with activation exponents in [-1, 1]: the products span < 40 bits, so the
+    float64 oracle must equal the exact rational sums of bf16 x NVFP4 products."""
+    rng = np.random.default_rng(31)
+    E, N, K = 3, 4, 64
+    offsets = np.array([0, 1, 1, 4])             # expert 1 is empty
+    a = _bf16_rows(rng, 4, K)
+    W = [_rand_nvfp4(rng, N, K) for _ in range(E)]
+    acc = moe.grouped_gemm_w4a16(a, offsets, lambda e: W[e], N, K)
+    for e in range(E):
+        for i in range(offsets[e], offsets[e + 1]):
+            for n in range(N):
+                s = sum(_bf16_val(a[i, k]) * _val(W[e][0][n], W[e][1][n], k) for k in range(K))
+                assert Fraction(acc[i, n]) == s, (e, i, n)
+
+
+def test_w4a16_gemm_one_hot_activation_reads_back_a_weight_column():
+    """x = 1.0 at column k only: acc[n] is the NVFP4 weight value w(n, k), decoded by hand."""
+    rng = np.random.default_rng(32)
+    N, K = 8, 64
+    W = _rand_nvfp4(rng, N, K)
+    cols = [0, 17, 63]
+    a = np.zeros((len(cols), K), np.uint16)
+    a[np.arange(len(cols)), cols] = 0x3F80              # bf16 1.0
+    acc = moe.grouped_gemm_w4a16(a, np.array([0, len(cols)]), lambda e: W, N, K)
+    for i, k in enumerate(cols):
+        for n in range(N):
+            assert Fraction(acc[i, n]) == _val(W[0][n], W[1][n], k)
+
+
+def test_w4a16_equals_w4a4_on_activations_nvfp4_represents_exactly():
+    """When each activation is exactly an NVFP4 value with row global 1 (a code times a
+    power-of-two block scale), the two arithmetics meet: W4A16 over those bf16 values equals
+    W4A4 over the same codes (two independently pinned GEMMs)."""
+    rng = np.random.default_rng(33)
+    N, K, R = 6, 128, 3
+    codes = rng.integers(0, 16, (R, K)).astype(np.uint8)
+    sc = rng.integers(0x30, 0x40, (R, K // 16)).astype(np.uint8) & 0x78   # powers of two
+    aq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    vals = nvfp4.dequantize(aq, sc)
+    bits = nvfp4.f64_to_bf16_bits(vals)
+    assert np.array_equal(nvfp4.bf16_bits_to_f32(bits).astype(np.float64), vals)  # exact in bf16
+    W = _rand_nvfp4(rng, N, K)
+    off = np.array([0, R])
+    assert np.array_equal(moe.grouped_gemm_w4a16(bits, off, lambda e: W, N, K),
+                          moe.grouped_gemm(aq, sc, off, lambda e: W, N, K))
+
+
+def test_w4a16_gemm_scales_exactly_with_the_activations():
+    """Doubling every bf16 activation doubles every output exactly."""
+    rng = np.random.default_rng(34)
+    N, K = 5, 256
+    a = _bf16_rows(rng, 2, K, -3, 3)
+    a2 = (a.astype(np.int64) + (1 << 7)).astype(np.uint16)     # exponent + 1
+    W = _rand_nvfp4(rng, N, K)
+    off = np.array([0, 2])
+    acc = moe.grouped_gemm_w4a16(a, off, lambda e: W, N, K)
+    assert np.array_equal(moe.grouped_gemm_w4a16(a2, off, lambda e: W, N, K), 2 * acc)
+
+
+def _run_w4a16(d, sel=None):
+    T = d["x"].shape[0]
+    idx = np.arange(len(d["a_expert"])) if sel is None else sel
+    return moe.layer_forward_w4a16(d["x"], d["a_expert"][idx], d["a_src"][idx], d["a_dst"][idx],
+                                   d["a_w"][idx], T, lambda e: d["W13"][e], lambda e: d["W2"][e],
+                                   *d["g"], d["E"], d["H"], d["I"])
+
+
+def test_w4a16_layer_single_row_closed_form():
+    """One token routed to one expert with weight 0.5: out = bf16(0.5 * g_down * W2 @ h),
+    h = bf16(silu(g_gate * Wg @ x) * g_up * Wu @ x), written out with exact rationals for
+    the GEMMs and the logistic function in float64 (no oracle code)."""
+    rng = np.random.default_rng(35)
+    E, H, I = 2, 32, 16
+    x = _bf16_rows(rng, 1, H)
+    W13 = [_rand_nvfp4(rng, 2 * I, H, 0x28, 0x38) for _ in range(E)]
+    W2 = [_rand_nvfp4(rng, H, I, 0x28, 0x38) for _ in range(E)]
+    gg, gu, gd = (np.full(E, v, np.float32) for v in (0.75, 0.5, 0.25))
+    out = moe.layer_forward_w4a16(x, np.array([1]), np.array([0]), np.array([0]),
+                                  np.array([0.5], np.float32), 1, lambda e: W13[e],
+                                  lambda e: W2[e], gg, gu, gd, E, H, I)
+    xv = [_bf16_val(x[0, k]) for k in range(H)]
+    zg = [float(0.75 * sum(xv[k] * _val(W13[1][0][j], W13[1][1][j], k) for k in range(H)))
+          for j in range(I)]
+    zu = [float(0.5 * sum(xv[k] * _val(W13[1][0][I + j], W13[1][1][I + j], k) for k in range(H)))
+          for j in range(I)]
+    h = nvfp4.f64_to_bf16_bits(np.array([g / (1.0 + np.exp(-g)) * u for g, u in zip(zg, zu)]))
+    hv = [_bf16_val(b) if b & 0x7FFF else Fraction(0) for b in h]
+    y = [float(Fraction(1, 8) * sum(hv[j] * _val(W2[1][0][n], W2[1][1][n], j) for j in range(I)))
+         for n in range(H)]
+    assert np.array_equal(out[0], nvfp4.f64_to_bf16_bits(np.array(y)))
+
+
+def test_w4a16_layer_batch_parity_and_determinism():
+    """[GG] "Proof" in W4A16 arithmetic: a token alone equals the token in its batch."""
+    d = _tiny_layer_inputs(23)
+    full = _run_w4a16(d)
+    assert np.array_equal(_run_w4a16(d), full)
+    k = d["k"]
+    for t in (1, 4):
+        alone = _run_w4a16(d, np.arange(t * k, t * k + k))
+        assert np.array_equal(alone[t], full[t])

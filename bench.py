@@ -12,11 +12,15 @@ measured on MI355X, the layer runs up to 10% slower during the first few hundred
 work after the GPU was idle).
 
 Metric (the pages' own byte model, table "Bytes decide it before the kernel runs" of the
-2026-09-06 page): weight-stream GB/s = active experts x 14,155,776 B / layer time.
+[MF]): weight-stream GB/s = active experts x 14,155,776 B / layer time.
 
 Prints ONE JSON line.  Also times the dominant kernel (the w13 grouped GEMM) with HIP
 events on its own stream over a loop of launches on the layer's real inputs, and the CPU
 oracle on a bounded sample of the same workload (cpu_baseline).
+
+[GG] is the page "The CUTLASS grouped GEMM beats the scalar GEMV loop at every M, M=1
+included, so the crossover is 1"; [MF] the page "Fusing the MoE layer's two grouped GEMMs is
+worth 4%, and a CUDA graph already collects it" (gabewillen.github.io/rocket).
 """
 import argparse
 import json

@@ -2,8 +2,8 @@
  *
  * The library implements the routed-expert loop that the page "The CUTLASS grouped GEMM
  * beats the scalar GEMV loop at every M, M=1 included, so the crossover is 1"
- * (gabewillen.github.io/rocket, posts/runtime, 2026-09-07) lays out in its section
- * "What changed":
+ * (gabewillen.github.io/rocket, posts/runtime; cited below as [GG]) lays out in its
+ * section "What changed":
  *
  *   gather -> NVFP4 quantize -> grouped GEMM over the fused gate|up weights (w13)
  *   -> SwiGLU with separate gate / up globals -> NVFP4 quantize -> grouped GEMM over w2
@@ -28,7 +28,7 @@
  *   outputs (no floating-point atomics anywhere).
  *
  * NVFP4 (page "Fusing the MoE layer's two grouped GEMMs is worth 4%, and a CUDA graph
- * already collects it", gabewillen.github.io/rocket, posts/kernels, 2026-09-06, table
+ * already collects it", gabewillen.github.io/rocket, posts/kernels, cited below as [MF]; table
  * "Bytes decide it before the kernel runs" and section "Different globals on the two
  * halves"): e2m1 elements, two per byte with the even element in the low nibble; one
  * e4m3fn scale byte per 16 consecutive elements along K; one fp32 global per activation
@@ -66,8 +66,8 @@ enum { MOE_ERR_EXPERT = 1, MOE_ERR_SRC = 2, MOE_ERR_DST = 4 };
 /* ----------------------------------------------------------------------------------
  * Weight packing (load time).  The grouped GEMM reads expert weights in a layout of
  * this library's own, written once when the weights are loaded — the counterpart of
- * the expert-cache fill in section "The seam CUTLASS forced open" of the 2026-09-07
- * page, which writes the scale layout its GEMM needs once per projection.
+ * the expert-cache fill in section "The seam CUTLASS forced open" of [GG], which writes
+ * the scale layout its GEMM needs once per projection.
  *
  * nvfp4_packed_weight_bytes: host query, bytes of the packed form of E matrices of
  *   [N, K] (exactly E*N*K*9/16: no padding).  Returns 0 if the shape is unsupported.
@@ -95,7 +95,7 @@ int nvfp4_unpack_weights(const void* packed, int E, int N, int K,
 
 /* ----------------------------------------------------------------------------------
  * moe_gather_rows — group assignments by expert and gather their activation rows.
- * Source: 2026-09-07 page, section "What changed": one row per (stream, expert) is
+ * Source: [GG], section "What changed": one row per (stream, expert) is
  * gathered, and rows are grouped by expert id across the batch in ascending id order
  * (an ordered map), so group order depends only on which experts fired.
  *
@@ -124,7 +124,7 @@ int moe_gather_rows(const uint16_t* x, int S, int H,
 
 /* ----------------------------------------------------------------------------------
  * nvfp4_quantize_rows — NVFP4-quantize each bf16 row with its own fp32 global.
- * Source: 2026-09-07 page, section "What changed" (the two quantize steps; the FP4
+ * Source: [GG], section "What changed" (the two quantize steps; the FP4
  * tensor-core GEMM takes FP4 on both operands, section "Numbers").  The pages give no
  * quantizer formula; this one is the two-level NVFP4 reading, in float32, in this order:
  *   amax = max|x|; gs = amax / 2688 (1 if amax == 0)                 [2688 = 6 * 448]
@@ -145,7 +145,7 @@ int nvfp4_quantize_rows(const uint16_t* in, int R, int K,
  * grouped_gemm_nvfp4 — out[i, n] = sum_k a(i, k) * w_e(n, k) for every row i of every
  * expert group e, with a = e2m1(aq) * e4m3(as) and w = e2m1 * e4m3 of expert e's packed
  * weights; no globals (alpha = 1).
- * Source: 2026-09-07 page, section "What changed": grouped GEMM w13 (N = 2I = 4096,
+ * Source: [GG], section "What changed": grouped GEMM w13 (N = 2I = 4096,
  * K = H = 4096, fused gate|up) and w2 (N = H, K = I), alpha = 1.
  *
  * aq [R, K/2], as [R, K/16]: NVFP4 activation rows (as written by nvfp4_quantize_rows).
@@ -162,10 +162,29 @@ int grouped_gemm_nvfp4(const uint8_t* aq, const uint8_t* as, const int32_t* expe
                        int flags, int gemv_max_rows, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------------
+ * grouped_gemm_w4a16 — out[i, n] = sum_k x(i, k) * w_e(n, k) for every row i of every
+ * expert group e, with x the bf16 activation values taken exactly (no quantization) and
+ * w = e2m1 * e4m3 of expert e's packed weights; no globals (alpha = 1).
+ * Source: [GG], section "Numbers": the dequant-GEMV path computes W4A16, exact BF16
+ * activations against an NVFP4 weight; here that arithmetic runs as a grouped GEMM over
+ * the same packed weights as grouped_gemm_nvfp4.
+ *
+ * a [R, K] bf16: the grouped activation rows.  expert_offsets [E+1] (device), w_packed as
+ * for grouped_gemm_nvfp4, out [R, N] float.  Rows outside every group are not written.
+ * Every group runs on the bf16 matrix cores; the products are exact and accumulate in
+ * fp32 in an order fixed by (N, K) alone, so a row's output does not depend on the other
+ * rows of its group or batch.
+ * Limits: N % 16 == 0, K % 128 == 0, K <= 4096, R * K * 2 < 2^31, E <= 8192, 16-byte
+ * aligned pointers.
+ * ---------------------------------------------------------------------------------- */
+int grouped_gemm_w4a16(const uint16_t* a, const int32_t* expert_offsets, int E, int R,
+                       const void* w_packed, int N, int K, float* out, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
  * swiglu_grouped — h[i, j] = bf16( silu(zg) * zu ), for row i of expert e:
  *   zg = row_gs[i] * g_gate[e] * acc13[i, j],  zu = row_gs[i] * g_up[e] * acc13[i, I + j].
- * Source: 2026-09-07 page, section "What changed" (per-group gate/up weight_scale_2
- * applied in the SwiGLU kernel); 2026-09-06 page, section "Different globals on the two
+ * Source: [GG], section "What changed" (per-group gate/up weight_scale_2
+ * applied in the SwiGLU kernel); [MF], section "Different globals on the two
  * halves", option (a).  row_gs is the activation row global of the w13 GEMM's input.
  *
  * acc13 [R, 2I] float (gate in columns [0, I), up in [I, 2I)), expert_offsets [E+1],
@@ -179,7 +198,7 @@ int swiglu_grouped(const float* acc13, int R, int I, const int32_t* expert_offse
 /* ----------------------------------------------------------------------------------
  * moe_scatter_add — out[t] = bf16( sum over p in [tok_off[t], tok_off[t+1]) of
  *   row_w[i] * g_down[e_i] * row_gs[i] * y[i] ),  i = tok_rows[p].
- * Source: 2026-09-07 page, section "What changed" (scatter-add weighted by router weight
+ * Source: [GG], section "What changed" (scatter-add weighted by router weight
  * * down weight_scale_2) and section "Proof" (shared accumulator row, accumulated in
  * order of i).  row_gs is the activation row global of the w2 GEMM's input.
  *
@@ -196,7 +215,7 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
 
 /* ----------------------------------------------------------------------------------
  * moe_layer_forward — the whole routed-expert layer: every step above, in order, on
- * one stream, with no host synchronization (2026-09-07 page, section "What changed").
+ * one stream, with no host synchronization ([GG], section "What changed").
  * The S source rows are quantized once each, in the same launch as the grouping, and the
  * w13 GEMM reads grouped row i from source row row_src[i] (a row's codes depend only on
  * the row, so this equals gather-then-quantize); the second quantize is fused into
@@ -228,6 +247,23 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S,
                       const float* a_w, int R, int T, uint16_t* out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ----------------------------------------------------------------------------------
+ * moe_layer_forward_w4a16 — the routed-expert layer in W4A16 arithmetic: the steps of
+ * moe_layer_forward without the two activation quantizations ([GG], section "Numbers":
+ * W4A16 is the arithmetic of the dequant-GEMV path).  Grouping; the w13 GEMM over the
+ * bf16 source rows (grouped row i reads source row row_src[i]) with SwiGLU in its
+ * epilogue, h = bf16( silu(g_gate[e] * acc_gate) * g_up[e] * acc_up ) (bf16 activations
+ * carry no row global); the w2 GEMM over bf16 h; the scatter-add weighted by
+ * row_w[i] * g_down[e].
+ * Same descriptor (flags and gemv_max_rows are not used: every group runs on the bf16
+ * matrix cores), arguments, workspace (moe_layer_workspace_bytes) and error word as
+ * moe_layer_forward.  Limits: those of moe_layer_forward, plus H <= 4096 and I <= 4096.
+ * ---------------------------------------------------------------------------------- */
+int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
+                            const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
+                            const float* a_w, int R, int T, uint16_t* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Synchronizes `stream`, then returns the device error word at `err_word` (the
  * err_word of moe_gather_rows, or a moe_layer_forward workspace), or a negative
  * moe_status if the read fails. */
@@ -239,7 +275,7 @@ const char* moe_last_error(void);
 
 /* Host string: hash of the sources this library was built from.  Bindings compare it
  * with the sources on disk so that a stale build is refused instead of silently run
- * (the 2026-09-07 page, section "A debugging note", lost a day to a stale test binary). */
+ * ([GG], section "A debugging note", lost a day to a stale test binary). */
 const char* moe_source_hash(void);
 
 #ifdef __cplusplus

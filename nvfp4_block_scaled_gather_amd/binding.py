@@ -54,11 +54,14 @@ _SIGNATURES = {
                              _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "nvfp4_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "grouped_gemm_nvfp4": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _P, _I, _I, _P]),
+    "grouped_gemm_w4a16": (_I, [_P, _P, _I, _I, _P, _I, _I, _P, _P]),
     "swiglu_grouped": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _P]),
     "moe_scatter_add": (_I, [_P, _I, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P, _P]),
     "moe_layer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MoeLayerDesc), _I, _I, _I]),
     "moe_layer_forward": (_I, [ctypes.POINTER(MoeLayerDesc), _P, _I, _P, _P, _P, _P, _I, _I,
                                _P, _P, ctypes.c_size_t, _P]),
+    "moe_layer_forward_w4a16": (_I, [ctypes.POINTER(MoeLayerDesc), _P, _I, _P, _P, _P, _P, _I,
+                                     _I, _P, _P, ctypes.c_size_t, _P]),
     "moe_get_device_error": (_I, [_P, _P]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_source_hash": (ctypes.c_char_p, []),
@@ -142,6 +145,11 @@ def grouped_gemm_nvfp4(aq, as_, expert_offsets, E, R, w_packed, N, K, out,
         flags, gemv_max_rows, _stream(stream)))
 
 
+def grouped_gemm_w4a16(a, expert_offsets, E, R, w_packed, N, K, out, stream=None):
+    _check("grouped_gemm_w4a16", load().grouped_gemm_w4a16(
+        _ptr(a), _ptr(expert_offsets), E, R, _ptr(w_packed), N, K, _ptr(out), _stream(stream)))
+
+
 def swiglu_grouped(acc13, R, I, expert_offsets, E, g_gate, g_up, row_gs, h, stream=None):
     _check("swiglu_grouped", load().swiglu_grouped(
         _ptr(acc13), R, I, _ptr(expert_offsets), E, _ptr(g_gate), _ptr(g_up), _ptr(row_gs),
@@ -168,6 +176,13 @@ def moe_layer_workspace_bytes(desc, S, R, T):
 def moe_layer_forward(desc, x, S, a_expert, a_src, a_dst, a_w, R, T, out, workspace,
                       workspace_bytes, stream=None):
     _check("moe_layer_forward", load().moe_layer_forward(
+        ctypes.byref(desc), _ptr(x), S, _ptr(a_expert), _ptr(a_src), _ptr(a_dst), _ptr(a_w), R, T,
+        _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def moe_layer_forward_w4a16(desc, x, S, a_expert, a_src, a_dst, a_w, R, T, out, workspace,
+                            workspace_bytes, stream=None):
+    _check("moe_layer_forward_w4a16", load().moe_layer_forward_w4a16(
         ctypes.byref(desc), _ptr(x), S, _ptr(a_expert), _ptr(a_src), _ptr(a_dst), _ptr(a_w), R, T,
         _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
 

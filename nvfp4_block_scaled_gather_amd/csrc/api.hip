@@ -41,6 +41,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 constexpr int kMaxGroupKeys = 16000;  // E + T, LDS histograms of the grouping kernel
 constexpr int kMaxRowK = 8192;        // row kernels keep a row in registers
 constexpr int kMaxE = 8192;
+constexpr int kMaxBf16K = 4096;       // W4A16: 16 staged bf16 rows of K must fit in LDS
 
 int check_group_args(const void* a_expert, const void* a_src, const void* a_dst, const void* a_w,
                      int R, int E, int S, int T, const void* expert_offsets, const void* row_src,
@@ -156,6 +157,18 @@ int grouped_gemm_nvfp4(const uint8_t* aq, const uint8_t* as, const int32_t* expe
                     "grouped GEMM launch");
 }
 
+int grouped_gemm_w4a16(const uint16_t* a, const int32_t* expert_offsets, int E, int R,
+                       const void* w_packed, int N, int K, float* out, hipStream_t stream) {
+  int st = check_gemm_args(a, a, expert_offsets, E, R, w_packed, N, K, out, MOE_PATH_FORCE_MFMA, 0);
+  if (st != MOE_OK) return st;
+  REQUIRE(K <= kMaxBf16K, MOE_EUNSUPPORTED, "W4A16 GEMM: K=%d exceeds %d", K, kMaxBf16K);
+  REQUIRE((long long)R * K * 2 < (1ll << 31), MOE_EUNSUPPORTED,
+          "W4A16 GEMM: activations of %d rows x %d columns exceed 2 GiB", R, K);
+  return hip_status(moe::launch_grouped_gemm_w4a16(a, nullptr, R, expert_offsets, E, R,
+                                                   (const uint8_t*)w_packed, N, K, out, stream),
+                    "W4A16 grouped GEMM launch");
+}
+
 int swiglu_grouped(const float* acc13, int R, int I, const int32_t* expert_offsets, int E,
                    const float* g_gate, const float* g_up, const float* row_gs, uint16_t* h,
                    hipStream_t stream) {
@@ -204,6 +217,7 @@ struct LayerWs {
   uint8_t* hq;
   uint8_t* hs;
   float* hgs;
+  uint16_t* h16;  // W4A16: h [R, I] bf16 (the w2 GEMM's input while acc takes its output)
   size_t bytes;
 };
 
@@ -232,6 +246,7 @@ LayerWs carve(const moe_layer_desc* L, int S, int R, int T, uint8_t* base) {
   w.hq = take(r * L->I / 2);
   w.hs = take(r * L->I / 16);
   w.hgs = (float*)take(4 * r);
+  w.h16 = (uint16_t*)take(2 * r * L->I);
   w.bytes = o;
   return w;
 }
@@ -315,6 +330,45 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
                                  (const uint8_t*)L->w2_packed, H, I, w.acc, L->flags,
                                  L->gemv_max_rows, stream, w.row_w, L->g_down, w.hgs);
     if (e != hipSuccess) return hip_status(e, "layer: w2 GEMM launch");
+  }
+  e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
+  return hip_status(e, "layer: scatter launch");
+}
+
+int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
+                            const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
+                            const float* a_w, int R, int T, uint16_t* out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  int st = check_layer(L, S, R, T);
+  if (st != MOE_OK) return st;
+  REQUIRE(L->H <= kMaxBf16K && L->I <= kMaxBf16K, MOE_EUNSUPPORTED,
+          "W4A16 layer: H=%d and I=%d must be <= %d", L->H, L->I, kMaxBf16K);
+  REQUIRE((long long)(S > R ? S : R) * (L->H > L->I ? L->H : L->I) * 2 < (1ll << 31),
+          MOE_EUNSUPPORTED, "W4A16 layer: bf16 activations exceed 2 GiB");
+  REQUIRE(L->w13_packed && L->w2_packed && L->g_gate && L->g_up && L->g_down, MOE_EINVAL,
+          "layer: null weights / globals");
+  REQUIRE(workspace && aligned(workspace, 256), MOE_EINVAL, "layer: workspace null or not 256-byte aligned");
+  const LayerWs w = carve(L, S, R, T, (uint8_t*)workspace);
+  REQUIRE(workspace_bytes >= w.bytes, MOE_EWORKSPACE, "layer: workspace %zu bytes < %zu needed",
+          workspace_bytes, w.bytes);
+  if (R > 0) REQUIRE(a_expert && a_src && a_dst && a_w, MOE_EINVAL, "layer: null assignment array");
+  if (R > 0 && S > 0) REQUIRE(x, MOE_EINVAL, "layer: null x");
+  if (T > 0) REQUIRE(out, MOE_EINVAL, "layer: null out");
+  REQUIRE(aligned(x, 16) && aligned(out, 8) && aligned(L->w13_packed, 16) && aligned(L->w2_packed, 16),
+          MOE_EINVAL, "layer: x / weights must be 16-byte, out 8-byte aligned");
+  const int E = L->E, H = L->H, I = L->I;
+  hipError_t e = moe::launch_group(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
+                                   w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, stream);
+  if (e != hipSuccess) return hip_status(e, "layer: group launch");
+  if (R > 0) {
+    e = moe::launch_grouped_gemm_swiglu_w4a16(x, w.row_src, S, w.offsets, E, R,
+                                              (const uint8_t*)L->w13_packed, I, H, L->g_gate,
+                                              L->g_up, w.h16, stream);
+    if (e != hipSuccess) return hip_status(e, "layer: W4A16 w13 GEMM + SwiGLU launch");
+    e = moe::launch_grouped_gemm_w4a16(w.h16, nullptr, R, w.offsets, E, R,
+                                       (const uint8_t*)L->w2_packed, H, I, w.acc, stream, w.row_w,
+                                       L->g_down);
+    if (e != hipSuccess) return hip_status(e, "layer: W4A16 w2 GEMM launch");
   }
   e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
   return hip_status(e, "layer: scatter launch");

@@ -14,6 +14,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 
@@ -53,6 +55,26 @@ __device__ __forceinline__ uint32_t e2m1_encode(float q) {
   const uint32_t b = __float_as_uint(__builtin_fmaxf(a, 1.0f));
   const uint32_t nrm = min(((b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22) - 252u, 7u);  // 2..7
   return (sub + nrm - 2u) | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+// Eight e2m1 nibbles (one 32-bit word, element 2k in the low nibble of byte k) times a
+// non-negative block scale given as a float -> 8 exact bf16 values in element order (W4A16
+// weights).  Each nibble pair converts to float exactly, the product with the e4m3 scale
+// has at most 6 significant bits (exact in float), and its upper 16 bits are then the bf16
+// value itself.
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float scale) {
+  const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  const f32x2 pp[4] = {p0, p1, p2, p3};
+  u32x4 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float lo = pp[b][0] * scale, hi = pp[b][1] * scale;
+    r[b] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+  }
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // bf16 <-> float
@@ -287,6 +309,17 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, cons
                                       const uint8_t* w13, int I, int K, const float* g_gate,
                                       const float* g_up, const float* row_gs,
                                       const int32_t* gs_map, uint16_t* h, hipStream_t s);
+// W4A16 (bf16 activation rows ab [a_rows, K], through amap): the grouped GEMM (with c_w,
+// rows multiplied by c_w[i] * c_g[e]) and the w13 GEMM with the SwiGLU epilogue (gate / up
+// globals alone).
+hipError_t launch_grouped_gemm_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
+                                     const int32_t* expert_offsets, int E, int R, const uint8_t* w,
+                                     int N, int K, float* out, hipStream_t s,
+                                     const float* c_w = nullptr, const float* c_g = nullptr);
+hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
+                                            const int32_t* expert_offsets, int E, int R,
+                                            const uint8_t* w13, int I, int K, const float* g_gate,
+                                            const float* g_up, uint16_t* h, hipStream_t s);
 // Grouping and NVFP4 quantization of the S source rows of x in one launch (independent
 // work: block 0 groups, the other blocks quantize four rows each).
 hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,

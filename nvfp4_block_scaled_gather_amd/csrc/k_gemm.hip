@@ -78,7 +78,9 @@ struct GemmArgs {
   // activation global), the term the scatter-add sums.
   const float* c_w;
   const float* c_g;
-  const float* c_gs;
+  const float* c_gs;       // nullptr: 1 (bf16 activations carry no row global)
+  // W4A16: bf16 activation rows [a_rows, K] (through amap) in place of aq / as
+  const uint16_t* ab;
 };
 
 // ------------------------------------------------------------------------- LDS layout
@@ -88,13 +90,17 @@ struct GemmArgs {
 __host__ __device__ __forceinline__ int act_list_bytes(int E) { return (2 * E + 15) & ~15; }
 __host__ __device__ __forceinline__ int q_stride(int K) { return K / 2 + 16; }
 __host__ __device__ __forceinline__ int s_stride(int K) { return K / 16 + 8; }
-// The staging area also holds the MFMA epilogue's output block (at most 16 rows x 132
-// floats: 128 columns of two tiles per wave, plus padding), which for small K is larger
-// than the staged rows.
-constexpr int kOutBlockBytes = kPassRows * 132 * 4;
-static size_t gemm_lds_bytes(int E, int K, int rows) {
-  const size_t stage = (size_t)rows * (q_stride(K) + s_stride(K));
-  return (size_t)act_list_bytes(E) + (stage > (size_t)kOutBlockBytes ? stage : (size_t)kOutBlockBytes);
+// bf16 activation rows (W4A16): 2K bytes, padded the same way.
+__host__ __device__ __forceinline__ int b_stride(int K) { return 2 * K + 16; }
+// The staging area also holds the MFMA epilogue's output block (16 rows x the workgroup's
+// columns plus padding), which for small K is larger than the staged rows; 256 bytes of
+// slack keep the B-operand prefetch past the last chunk inside the allocation.
+static size_t out_block_bytes(int NS, int waves) { return (size_t)kPassRows * (16 * NS * waves + 4) * 4; }
+static size_t gemm_lds_bytes(int E, int K, int rows, bool abf = false, int NS = 2,
+                             int waves = kGemmWaves) {
+  const size_t stage = (size_t)rows * (abf ? b_stride(K) : q_stride(K) + s_stride(K));
+  const size_t outb = out_block_bytes(NS, waves);
+  return (size_t)act_list_bytes(E) + (stage > outb ? stage : outb) + 256;
 }
 
 // Ids of the experts whose group size is in [gmin, gmax], ascending, into LDS (wave 0).
@@ -134,30 +140,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Stage activation rows arow0 .. arow0 + nrows - 1 (through amap) into LDS with
-// buffer-to-LDS loads: wave w copies rows w, w + 4, ...; a row is K/2 nibble bytes in
-// 1 KiB pieces (16 bytes per lane) and K/16 scale bytes in 256-byte pieces (4 bytes per
-// lane).  The caller waits for the loads and synchronizes before reading.
+// buffer-to-LDS loads: wave w copies rows w, w + WAVES, ...; an NVFP4 row is K/2 nibble
+// bytes in 1 KiB pieces (16 bytes per lane) and K/16 scale bytes in 256-byte pieces (4
+// bytes per lane); a bf16 row (ABF) is 2K bytes in 1 KiB pieces.  The caller waits for the
+// loads and synchronizes before reading.
+template <bool ABF, int WAVES>
 __device__ __forceinline__ void stage_rows(const GemmArgs& p, int arow0, int nrows, uint8_t* s_q,
                                            uint8_t* s_s) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qb = p.K / 2, sb = p.K / 16;
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, p.a_rows * qb);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, p.a_rows * sb);
-  for (int row = wave; row < nrows; row += kGemmWaves) {
-    const int i = arow0 + row;
-    const int src = __builtin_amdgcn_readfirstlane(p.amap ? p.amap[i] : i);
-    uint8_t* dq = s_q + row * q_stride(p.K);
-    uint8_t* ds = s_s + row * s_stride(p.K);
-    for (int o = 0; o < qb; o += 1024) {
-      if (o + 16 * lane < qb)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(dq + o), 16, 16 * lane,
-                                                 src * qb + o, 0, 0);
+  if constexpr (ABF) {
+    const int rb = 2 * p.K;
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(p.ab, p.a_rows * rb);
+    for (int row = wave; row < nrows; row += WAVES) {
+      const int i = arow0 + row;
+      const int src = __builtin_amdgcn_readfirstlane(p.amap ? p.amap[i] : i);
+      uint8_t* db = s_q + row * b_stride(p.K);
+      for (int o = 0; o < rb; o += 1024) {
+        if (o + 16 * lane < rb)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)(db + o), 16, 16 * lane,
+                                                   src * rb + o, 0, 0);
+      }
     }
-    for (int o = 0; o < sb; o += 256) {
-      if (o + 4 * lane < sb)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(ds + o), 4, 4 * lane,
-                                                 src * sb + o, 0, 0);
+  } else {
+    const int qb = p.K / 2, sb = p.K / 16;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, p.a_rows * qb);
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, p.a_rows * sb);
+    for (int row = wave; row < nrows; row += WAVES) {
+      const int i = arow0 + row;
+      const int src = __builtin_amdgcn_readfirstlane(p.amap ? p.amap[i] : i);
+      uint8_t* dq = s_q + row * q_stride(p.K);
+      uint8_t* ds = s_s + row * s_stride(p.K);
+      for (int o = 0; o < qb; o += 1024) {
+        if (o + 16 * lane < qb)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(dq + o), 16, 16 * lane,
+                                                   src * qb + o, 0, 0);
+      }
+      for (int o = 0; o < sb; o += 256) {
+        if (o + 4 * lane < sb)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(ds + o), 4, 4 * lane,
+                                                   src * sb + o, 0, 0);
+      }
     }
   }
 }
@@ -250,12 +273,11 @@ __device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC
 // the epilogue writes h = SwiGLU(gate, up) as bf16 (ggate, gup: the expert's gate / up
 // weight globals) instead of the fp32 products.  Otherwise, with p.c_w, ggate is the
 // expert's down global of the scatter-ready epilogue.
-template <int NS, int D, int S, bool SWI>
+template <int NS, int D, int S, bool SWI, bool ABF, int WAVES>
 __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0,
                                           uint8_t* s_q, uint8_t* s_s, float ggate, float gup) {
   static_assert(!SWI || NS == 2, "the SwiGLU epilogue pairs one gate and one up tile");
-  static_assert(NS <= 2, "the output block in LDS holds two tiles per wave");
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, r = lane & 15;
   const int K = p.K, NC = K / 128;
@@ -270,81 +292,114 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, __builtin_amdgcn_readfirstlane(range));
   // scatter-ready epilogue: this lane's coefficient inputs, loaded now so the epilogue
   // does not wait on them
-  float ow = 0.f, ogs = 0.f;
+  float ow = 0.f, ogs = 1.f;
   if (!SWI && p.c_w && r < nrows) {
     ow = p.c_w[arow0 + r];
-    ogs = p.c_gs[arow0 + r];
+    if (p.c_gs) ogs = p.c_gs[arow0 + r];
   }
 
-  stage_rows(p, arow0, nrows, s_q, s_s);
+  stage_rows<ABF, WAVES>(p, arow0, nrows, s_q, s_s);
   __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
   __syncthreads();
 
   const int rl = r < nrows ? r : 0;
-  const uint8_t* aq_l = s_q + rl * q_stride(K) + 16 * kq;
-  const uint8_t* as_l = s_s + rl * s_stride(K) + 2 * kq;
   f32x4 acc[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // The B operand of chunk c is read from LDS while chunk c - 1 is computed (reads one
-  // chunk past the end land in the row padding or the next region: never used).
-  u32x4 an_next = *(const u32x4*)aq_l;
-  uint32_t asc_next = *(const uint16_t*)as_l;
-  stream_weights<NS, D, S>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
-                           [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
-    const u32x4 an = an_next;
-    const uint32_t asc = asc_next;
-    an_next = *(const u32x4*)(aq_l + 64 * (c + 1));
-    asc_next = *(const uint16_t*)(as_l + 8 * (c + 1));
-    __builtin_amdgcn_sched_barrier(0);  // issue the reads before this chunk's work
-    const uint32_t sa = scale_pair_signed(asc);
-    f16x8 bop[4];
+  if constexpr (ABF) {
+    // W4A16: the B operand is the staged bf16 row as it is, with the weights' k
+    // assignment (lane: row r; MFMA q of a chunk takes the 8 k at 32 kq + 8 q), the A
+    // operand the weights dequantized exactly to bf16.
+    const uint8_t* ab_l = s_q + rl * b_stride(K) + 64 * kq;
+    u32x4 b_next[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bop[q] = dequant8(an[q], sa, q >= 2);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint32_t sw = scale_pair_pos(sg[s][j >> 1], (j & 1) ? 0x0c030c02u : 0x0c010c00u);
+    for (int q = 0; q < 4; ++q) b_next[q] = *(const u32x4*)(ab_l + 16 * q);
+    stream_weights<NS, D, S>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
+                             [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
+      u32x4 bq[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f16x8 aop = dequant8(wn[s][q], sw, q >= 2);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[q], acc[s], 0, 0, 0);
+        bq[q] = b_next[q];
+        b_next[q] = *(const u32x4*)(ab_l + 256 * (c + 1) + 16 * q);
       }
-    }
-  });
+      __builtin_amdgcn_sched_barrier(0);  // issue the reads before this chunk's work
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint32_t ws = chunk_scales(sg[s], j);
+        const float f0 = e4m3_to_f32(ws & 0xFFu), f1 = e4m3_to_f32(ws >> 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x8 aop = dequant8_bf16(wn[s][q], q >= 2 ? f1 : f0);
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bq[q]),
+                                                           acc[s], 0, 0, 0);
+        }
+      }
+    });
+  } else {
+    const uint8_t* aq_l = s_q + rl * q_stride(K) + 16 * kq;
+    const uint8_t* as_l = s_s + rl * s_stride(K) + 2 * kq;
+    // The B operand of chunk c is read from LDS while chunk c - 1 is computed (reads one
+    // chunk past the end land in the row padding, the next region or the slack: never used).
+    u32x4 an_next = *(const u32x4*)aq_l;
+    uint32_t asc_next = *(const uint16_t*)as_l;
+    stream_weights<NS, D, S>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
+                             [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
+      const u32x4 an = an_next;
+      const uint32_t asc = asc_next;
+      an_next = *(const u32x4*)(aq_l + 64 * (c + 1));
+      asc_next = *(const uint16_t*)(as_l + 8 * (c + 1));
+      __builtin_amdgcn_sched_barrier(0);  // issue the reads before this chunk's work
+      const uint32_t sa = scale_pair_signed(asc);
+      f16x8 bop[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bop[q] = dequant8(an[q], sa, q >= 2);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const uint32_t sw = scale_pair_pos(sg[s][j >> 1], (j & 1) ? 0x0c030c02u : 0x0c010c00u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f16x8 aop = dequant8(wn[s][q], sw, q >= 2);
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[q], acc[s], 0, 0, 0);
+        }
+      }
+    });
+  }
 
   // Lane l holds out row r x weight rows 4 kq .. 4 kq + 3 of each tile.  The workgroup's
-  // output block (its rows x 128 columns, or x 64 h columns) is assembled in LDS over the
-  // staged rows and written as whole rows, so every store covers full 128-byte lines
-  // (written from the lanes directly, each line arrived in 32- or 64-byte pieces from
-  // four waves).
+  // output block (its rows x 16 NS WAVES columns, or x 16 WAVES h columns) is assembled in
+  // LDS over the staged rows and written as whole rows, so every store covers full
+  // 128-byte lines (written from the lanes directly, each line arrived in 32- or 64-byte
+  // pieces from several waves).
   const int wave = threadIdx.x >> 6;
   __syncthreads();  // every wave is done with the staged rows: reuse them for the output
   if (SWI) {
-    uint16_t* so = (uint16_t*)s_q;  // [16][72] bf16 (within kOutBlockBytes)
+    constexpr int WCH = 16 * WAVES;            // h columns of the workgroup
+    constexpr int LPR = WCH / 8;               // 16-byte pieces per row
+    uint16_t* so = (uint16_t*)s_q;             // [16][WCH + 8] bf16 (within the output block)
     if (r < nrows && nsv > 0) {
       const int i = arow0 + r;
-      const float gs = p.row_gs[p.gs_map ? p.gs_map[i] : i];
+      const float gs = p.row_gs ? p.row_gs[p.gs_map ? p.gs_map[i] : i] : 1.0f;
       const float cg = gs * ggate, cu = gs * gup;
       uint32_t hb[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) hb[x] = swiglu_bf16(cg, acc[0][x], cu, acc[1][x]);
       const u32x2 v = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-      *(u32x2*)(so + r * 72 + wave * 16 + 4 * kq) = v;
+      *(u32x2*)(so + r * (WCH + 8) + wave * 16 + 4 * kq) = v;
     }
     __syncthreads();
     const int colW = col0 - 16 * wave;
-    const int rr = lane >> 3, c = (lane & 7) * 8;
-    for (int row = rr + 8 * wave; row < nrows; row += 32) {
+    for (int u = threadIdx.x; u < nrows * LPR; u += 64 * WAVES) {
+      const int row = u / LPR, c = (u % LPR) * 8;
       if (colW + c < p.I) {
-        const u32x4 v = *(const u32x4*)(so + row * 72 + c);
+        const u32x4 v = *(const u32x4*)(so + row * (WCH + 8) + c);
         __builtin_nontemporal_store(v, (u32x4*)(p.h + (size_t)(arow0 + row) * p.I + colW + c));
       }
     }
   } else {
-    constexpr int WC = 16 * NS * kGemmWaves;  // the workgroup's output columns
-    constexpr int LPR = WC / 4, RPI = 64 / LPR;  // lanes per row, rows per store
-    float* so = (float*)s_q;  // [16][WC + 4] floats (within kOutBlockBytes)
+    constexpr int WC = 16 * NS * WAVES;        // the workgroup's output columns
+    constexpr int LPR = WC / 4;                // 16-byte pieces per row
+    float* so = (float*)s_q;                   // [16][WC + 4] floats (the output block)
     if (r < nrows) {
       const float cf = ow * ggate * ogs;  // ggate: the expert's down global here
 #pragma unroll
@@ -361,8 +416,8 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     }
     __syncthreads();
     const int colW = col0 - 16 * NS * wave;
-    const int rr = lane / LPR, c = (lane % LPR) * 4;
-    for (int row = rr + RPI * wave; row < nrows; row += RPI * kGemmWaves) {
+    for (int u = threadIdx.x; u < nrows * LPR; u += 64 * WAVES) {
+      const int row = u / LPR, c = (u % LPR) * 4;
       if (colW + c < p.N) {
         const f32x4 v = *(const f32x4*)(so + row * (WC + 4) + c);
         __builtin_nontemporal_store(v, (f32x4*)(p.out + (size_t)(arow0 + row) * p.N + colW + c));
@@ -376,33 +431,33 @@ struct ItemLoop {
   int items_per_e, total, tiles, per_item;
 };
 
-__device__ __forceinline__ ItemLoop item_loop(const GemmArgs& p, int nact, int NS) {
+__device__ __forceinline__ ItemLoop item_loop(const GemmArgs& p, int nact, int NS, int waves) {
   ItemLoop L;
   L.tiles = p.N / 16;
-  L.per_item = kGemmWaves * NS;
+  L.per_item = waves * NS;
   L.items_per_e = (L.tiles + L.per_item - 1) / L.per_item;
   L.total = nact * L.items_per_e;
   return L;
 }
 
-template <int NS, int D, int S, bool SWI>
-__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
+template <int NS, int D, int S, bool SWI, bool ABF, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_nact;
   uint16_t* s_act = (uint16_t*)smem;
   const int nact = build_active_list(p, s_act, &s_nact);
   uint8_t* s_q = smem + act_list_bytes(p.E);
-  uint8_t* s_s = s_q + kPassRows * q_stride(p.K);
+  uint8_t* s_s = s_q + kPassRows * q_stride(p.K);  // NVFP4 scales (unused with ABF)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // SWI: a wave owns one gate tile (and the matching up tile)
   ItemLoop L;
   if (SWI) {
     L.tiles = p.I / 16;
-    L.per_item = kGemmWaves;
+    L.per_item = WAVES;
     L.items_per_e = (L.tiles + L.per_item - 1) / L.per_item;
     L.total = nact * L.items_per_e;
   } else {
-    L = item_loop(p, nact, NS);
+    L = item_loop(p, nact, NS, WAVES);
   }
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
@@ -417,8 +472,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs p) {
     const float gup = SWI ? p.g_up[e] : 0.f;
     for (int b = 0; b < G; b += kPassRows) {
       __syncthreads();  // the previous pass is done with the staged rows
-      mfma_pass<NS, D, S, SWI>(p, wt, nsv, r0 + b, min(kPassRows, G - b), 16 * t0, s_q, s_s,
-                               ggate, gup);
+      mfma_pass<NS, D, S, SWI, ABF, WAVES>(p, wt, nsv, r0 + b, min(kPassRows, G - b), 16 * t0,
+                                           s_q, s_s, ggate, gup);
     }
   }
 }
@@ -439,7 +494,7 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
   const __amdgpu_buffer_rsrc_t wr =
       make_rsrc(wt, __builtin_amdgcn_readfirstlane((nsv > 0 ? nsv : 0) * tstride));
 
-  stage_rows(p, arow0, nrows, s_q, s_s);
+  stage_rows<false, kGemmWaves>(p, arow0, nrows, s_q, s_s);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -507,7 +562,7 @@ __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
   uint8_t* s_q = smem + act_list_bytes(p.E);
   uint8_t* s_s = s_q + kGemvRows * q_stride(p.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const ItemLoop L = item_loop(p, nact, NS);
+  const ItemLoop L = item_loop(p, nact, NS, kGemmWaves);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
   for (int it = blockIdx.x; it < L.total; it += gridDim.x) {
@@ -547,27 +602,28 @@ static int gemm_grid(int per_item, const GemmArgs& a, int R) {
 constexpr int kSmallGridItems = 2048;
 
 template <class Kern>
-static hipError_t launch_one(Kern kern, int per_item, const GemmArgs& a, int rows, int R,
-                             hipStream_t s) {
-  const size_t lds = gemm_lds_bytes(a.E, a.K, rows);
+static hipError_t launch_one(Kern kern, int per_item, const GemmArgs& a, size_t lds, int threads,
+                             int R, hipStream_t s) {
   if (lds > 65536) {
     const hipError_t err = hipFuncSetAttribute((const void*)kern,
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(kern, dim3(gemm_grid(per_item, a, R)), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(gemm_grid(per_item, a, R)), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
 // The packed layout's scale group S fixes the kernel instance; the ring depth D is capped
 // at S.
-template <int NS, int D, bool SWI>
+template <int NS, int D, bool SWI, bool ABF = false, int WAVES = kGemmWaves>
 static hipError_t launch_mfma_t(const GemmArgs& a, int per, int R, hipStream_t s) {
+  const size_t lds = gemm_lds_bytes(a.E, a.K, kPassRows, ABF, NS, WAVES);
+  const int th = 64 * WAVES;
   switch (scale_group(a.K / 128)) {
-    case 8: return launch_one(k_gemm_mfma<NS, (D < 8 ? D : 8), 8, SWI>, per, a, kPassRows, R, s);
-    case 4: return launch_one(k_gemm_mfma<NS, (D < 4 ? D : 4), 4, SWI>, per, a, kPassRows, R, s);
-    case 2: return launch_one(k_gemm_mfma<NS, (D < 2 ? D : 2), 2, SWI>, per, a, kPassRows, R, s);
-    default: return launch_one(k_gemm_mfma<NS, 1, 1, SWI>, per, a, kPassRows, R, s);
+    case 8: return launch_one(k_gemm_mfma<NS, (D < 8 ? D : 8), 8, SWI, ABF, WAVES>, per, a, lds, th, R, s);
+    case 4: return launch_one(k_gemm_mfma<NS, (D < 4 ? D : 4), 4, SWI, ABF, WAVES>, per, a, lds, th, R, s);
+    case 2: return launch_one(k_gemm_mfma<NS, (D < 2 ? D : 2), 2, SWI, ABF, WAVES>, per, a, lds, th, R, s);
+    default: return launch_one(k_gemm_mfma<NS, 1, 1, SWI, ABF, WAVES>, per, a, lds, th, R, s);
   }
 }
 
@@ -583,11 +639,12 @@ static hipError_t launch_mfma(const GemmArgs& a, int R, hipStream_t s) {
 static hipError_t launch_gemv(const GemmArgs& a, int R, hipStream_t s) {
   const int per = kGemmWaves * MOE_GEMV_NS;
   constexpr int D = MOE_GEMV_D;
+  const size_t lds = gemm_lds_bytes(a.E, a.K, kGemvRows);
   switch (scale_group(a.K / 128)) {
-    case 8: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 8 ? D : 8), 8>, per, a, kGemvRows, R, s);
-    case 4: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 4 ? D : 4), 4>, per, a, kGemvRows, R, s);
-    case 2: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 2 ? D : 2), 2>, per, a, kGemvRows, R, s);
-    default: return launch_one(k_gemm_gemv<MOE_GEMV_NS, 1, 1>, per, a, kGemvRows, R, s);
+    case 8: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 8 ? D : 8), 8>, per, a, lds, 256, R, s);
+    case 4: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 4 ? D : 4), 4>, per, a, lds, 256, R, s);
+    case 2: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 2 ? D : 2), 2>, per, a, lds, 256, R, s);
+    default: return launch_one(k_gemm_gemv<MOE_GEMV_NS, 1, 1>, per, a, lds, 256, R, s);
   }
 }
 
@@ -635,6 +692,34 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+// ------------------------------------------------------------------------- W4A16
+// bf16 activations (2K bytes per staged row: 128 KiB for 16 rows at K = 4096) leave room
+// for one workgroup per CU, so the W4A16 instances run 16 waves per workgroup: the same 16
+// waves per CU stream weights against one shared copy of the staged rows.
+constexpr int kW4A16Waves = 16;
+
+hipError_t launch_grouped_gemm_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
+                                     const int32_t* off, int E, int R, const uint8_t* w, int N,
+                                     int K, float* out, hipStream_t s, const float* c_w,
+                                     const float* c_g) {
+  GemmArgs a{nullptr, nullptr, amap, a_rows, off, E, w, N, K, out, 1, 0x7FFFFFFF};
+  a.c_w = c_w;
+  a.c_g = c_g;
+  a.ab = ab;
+  return launch_mfma_t<2, MOE_GEMM_D, false, true, kW4A16Waves>(a, 2 * kW4A16Waves, R, s);
+}
+
+hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
+                                            const int32_t* off, int E, int R, const uint8_t* w13,
+                                            int I, int K, const float* g_gate, const float* g_up,
+                                            uint16_t* h, hipStream_t s) {
+  GemmArgs a{nullptr, nullptr, amap, a_rows, off, E, w13, 2 * I, K, nullptr, 1, 0x7FFFFFFF,
+             g_gate, g_up, nullptr, nullptr, h, I};
+  a.ab = ab;
+  // one gate tile per wave: (I/16)/16 items per expert, the grid of N = 2I with 32 per item
+  return launch_mfma_t<2, MOE_GEMM_D, true, true, kW4A16Waves>(a, 2 * kW4A16Waves, R, s);
 }
 
 }  // namespace moe

@@ -41,10 +41,16 @@ class DeviceLayer:
     """One layer's resident weights and descriptor for a ``workloads.Workload``."""
 
     def __init__(self, wl, device="cuda", flags=B.MOE_PATH_AUTO,
-                 gemv_max_rows=B.DEFAULT_GEMV_MAX_ROWS, experts=None, weights=None):
+                 gemv_max_rows=B.DEFAULT_GEMV_MAX_ROWS, experts=None, weights=None,
+                 arithmetic="w4a4"):
         """``weights``: already packed (w13, w2) device buffers of the same expert set
-        (workloads of one weight seed share them); otherwise they are packed here."""
+        (workloads of one weight seed share them); otherwise they are packed here.
+        ``arithmetic``: "w4a4" (moe_layer_forward: NVFP4 activations) or "w4a16"
+        (moe_layer_forward_w4a16: bf16 activations against the same weights)."""
         import torch
+        if arithmetic not in ("w4a4", "w4a16"):
+            raise ValueError("arithmetic must be 'w4a4' or 'w4a16', got %r" % (arithmetic,))
+        self.arithmetic = arithmetic
         self.wl = wl
         self.device = device
         if weights is None:
@@ -74,15 +80,16 @@ class DeviceLayer:
 
     def forward(self, stream=None):
         wl = self.wl
-        B.moe_layer_forward(self.desc, self.x, wl.S, self.a_expert, self.a_src, self.a_dst,
-                            self.a_w, wl.R, wl.T, self.out, self.ws_view, self.ws_bytes, stream)
+        fn = B.moe_layer_forward if self.arithmetic == "w4a4" else B.moe_layer_forward_w4a16
+        fn(self.desc, self.x, wl.S, self.a_expert, self.a_src, self.a_dst, self.a_w, wl.R, wl.T,
+           self.out, self.ws_view, self.ws_bytes, stream)
         return self.out
 
     def device_error(self):
         return B.moe_get_device_error(self.ws_view)
 
     def capture_graph(self):
-        """A HIP graph of one forward() (five kernel launches, no memset nodes); replaying
+        """A HIP graph of one forward() (its kernel launches, no memset nodes); replaying
         it recomputes self.out from the resident inputs.  Warmed up eagerly on the capture
         stream first."""
         import torch

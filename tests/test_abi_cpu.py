@@ -1,5 +1,10 @@
 """Host-side checks of the C ABI that need no GPU: the built library loads, exports every
-function the public header declares, and rejects bad arguments before launching."""
+function the public header declares, and rejects bad arguments before launching.
+
+[GG] is the page "The CUTLASS grouped GEMM beats the scalar GEMV loop at every M, M=1
+included, so the crossover is 1"; [MF] the page "Fusing the MoE layer's two grouped GEMMs is
+worth 4%, and a CUDA graph already collects it" (gabewillen.github.io/rocket).
+"""
 import ctypes
 import os
 import re
@@ -44,7 +49,7 @@ def test_library_is_fresh(lib):
 
 
 def test_packed_bytes_follow_the_page_byte_model(lib):
-    """Table "Bytes decide it before the kernel runs" (2026-09-06 page): 288 experts,
+    """Table "Bytes decide it before the kernel runs" ([MF]): 288 experts,
     w13 = 288*4096*4096*(0.5+1/16) = 2.718 GB, w2 = 1.359 GB, 4.077 GB total, a 13.5 MiB
     expert, 17.13 ms at 238 GB/s."""
     g = {}
@@ -114,6 +119,17 @@ def test_argument_errors_are_reported_before_launch(lib):
                                  need, null) == B.MOE_EUNSUPPORTED
     assert lib.moe_layer_forward(None, p16, 4, p16, p16, p16, p16, 8, 4, p16, ws, need, null) == B.MOE_EINVAL
     assert lib.moe_get_device_error(null, null) == B.MOE_EINVAL
+    # W4A16: K beyond what the staged bf16 rows fit in LDS, misalignment, H above 4096
+    assert lib.grouped_gemm_w4a16(p16, p16, 8, 4, p16, 64, 8192, p16, null) == B.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_w4a16(p16, p16, 8, 4, p16, 64, 100, p16, null) == B.MOE_EUNSUPPORTED
+    assert lib.grouped_gemm_w4a16(p8, p16, 8, 4, p16, 64, 128, p16, null) == B.MOE_EINVAL
+    wide = B.MoeLayerDesc(8, 8192, 128, 4096, 4096, 4096, 4096, 4096, 0, 0)
+    wneed = lib.moe_layer_workspace_bytes(ctypes.byref(wide), 4, 8, 4)
+    assert wneed > 0
+    assert lib.moe_layer_forward_w4a16(ctypes.byref(wide), p16, 4, p16, p16, p16, p16, 8, 4, p16,
+                                       ws, wneed, null) == B.MOE_EUNSUPPORTED
+    assert lib.moe_layer_forward_w4a16(ctypes.byref(d), p16, 4, p16, p16, p16, p16, 8, 4, p16, ws,
+                                       need - 1, null) == B.MOE_EWORKSPACE
 
 
 def test_workspace_grows_with_rows(lib):

@@ -4,6 +4,10 @@ Bit-exact: weight packing, grouping / gather indices, quantized nibbles / scale 
 row globals, and GEMMs whose every partial sum is exact.  Tolerances elsewhere:
 GEMM max |gpu - oracle| <= 2e-3 x row RMS (fp32 accumulation vs float64 over identical
 exact operands); SwiGLU and scatter within one bf16 rounding step.
+
+[GG] is the page "The CUTLASS grouped GEMM beats the scalar GEMV loop at every M, M=1
+included, so the crossover is 1"; [MF] the page "Fusing the MoE layer's two grouped GEMMs is
+worth 4%, and a CUDA graph already collects it" (gabewillen.github.io/rocket).
 """
 import numpy as np
 import pytest
@@ -100,7 +104,7 @@ def _to_bf16_bits(x):
 @pytest.mark.parametrize("K,R", [(64, 131), (16, 5), (256, 40), (2048, 24), (4096, 24), (8192, 4)])
 def test_quantize_bit_exact(lib, K, R):
     """K=64 with 131 rows is the shape of the page's kernel check (groups of 1 and 130
-    rows, 2026-09-07 page, section "Proof")."""
+    rows, [GG] "Proof")."""
     import torch
     from nvfp4_block_scaled_gather_amd import binding as B
     say("quantize K=%d R=%d" % (K, R))
@@ -316,7 +320,7 @@ def test_gemm_random_within_tolerance(lib, flags):
 
 @pytest.mark.parametrize("flags,sizes", [(1, [1, 2, 3, 4]), (2, [1, 5, 8, 16, 17, 33])])
 def test_gemm_row_invariance_within_path(lib, flags, sizes):
-    """2026-09-07 page, section "Proof": a row's output is the same alone or grouped."""
+    """[GG] "Proof": a row's output is the same alone or grouped."""
     from nvfp4_block_scaled_gather_amd import binding as B
     say("gemm row invariance", flags, sizes)
     rng = np.random.default_rng(60 + flags)
@@ -357,7 +361,7 @@ def test_gemm_grid_paths_agree_bitwise(lib, flags):
 
 @pytest.mark.parametrize("flags", [1, 2])
 def test_gemm_fused_w13_equals_separate_and_is_deterministic(lib, flags):
-    """2026-09-07 page, section "Proof": fused gate|up == gate-only and up-only GEMMs,
+    """[GG] "Proof": fused gate|up == gate-only and up-only GEMMs,
     and five repeated calls are bit-identical."""
     from nvfp4_block_scaled_gather_amd import binding as B
     say("gemm fused/determinism", flags)

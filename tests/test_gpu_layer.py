@@ -4,6 +4,10 @@ Tolerance (end to end): |gpu - oracle| <= 2% of the oracle row's RMS on >= 99.9%
 elements.  The two re-quantizations can flip a code where the GPU's fp32 and the oracle's
 float64 SwiGLU output round to different bf16 neighbours, so exact equality is not the
 bar here; it is for the layer against the same steps called one by one on the GPU.
+
+[GG] is the page "The CUTLASS grouped GEMM beats the scalar GEMV loop at every M, M=1
+included, so the crossover is 1"; [MF] the page "Fusing the MoE layer's two grouped GEMMs is
+worth 4%, and a CUDA graph already collects it" (gabewillen.github.io/rocket).
 """
 import numpy as np
 import pytest
@@ -105,7 +109,7 @@ def test_layer_equals_separate_calls(lib, flags, gemv_max):
 
 @pytest.mark.parametrize("flags", [1, 2])
 def test_layer_batch_parity_and_determinism(lib, flags):
-    """2026-09-07 page, section "Proof" / batch parity: a token's output is the same
+    """[GG] "Proof" / batch parity: a token's output is the same
     computed alone or inside the batch (within one GEMM path), and repeated calls are
     bit-identical."""
     from nvfp4_block_scaled_gather_amd import layer as L
@@ -223,6 +227,27 @@ def test_full_size_layer_sampled_tokens(lib, full_weights, name):
 
 
 # ------------------------------------------------------------------------------ HIP graph
+@pytest.mark.parametrize("name", ["decode8", "ragged570"])
+def test_full_size_w4a16_sampled_tokens(lib, full_weights, name):
+    """moe_layer_forward_w4a16 at full size on the resident expert set; the W4A16 oracle
+    recomputes every row of a few tokens."""
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    wl = W.make_workload(name)
+    say("full-size W4A16 layer", name, "R=%d" % wl.R)
+    dl = L.DeviceLayer(wl, weights=full_weights, arithmetic="w4a16")
+    got = host(dl.forward()).view(np.uint16).copy()
+    assert dl.device_error() == 0
+    tokens = _pick_tokens(wl, name)
+    sel = np.where(np.isin(wl.a_dst, tokens))[0]
+    want = omoe.layer_forward_w4a16(wl.x, wl.a_expert[sel], wl.a_src[sel], wl.a_dst[sel],
+                                    wl.a_w[sel], wl.T, wl.w13, wl.w2, wl.g_gate, wl.g_up,
+                                    wl.g_down, wl.E, wl.H, wl.I)[tokens]
+    frac, worst = _e2e_ok(got[tokens], want)
+    say("%s W4A16: fraction within tolerance %.5f, worst %.4f x RMS" % (name, frac, worst))
+    assert frac >= E2E_FRAC
+
+
 def test_graph_replay_matches_eager(lib):
     """A captured layer replays to the eager output bit for bit, replay after replay, with
     eager work between replays (no memset nodes are recorded)."""

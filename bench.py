@@ -57,6 +57,8 @@ def parse():
                    choices=["ragged570", "ragged2303", "zipf512", "decode1"])
     p.add_argument("--no-decode-sweep", action="store_true",
                    help="skip the decode-batch M sweep (M = 1 .. 32 token streams, top-8)")
+    p.add_argument("--no-w4a16", action="store_true",
+                   help="skip the W4A16 leg (bf16 activations against the same weights)")
     p.add_argument("--flush-mb", type=int, default=512,
                    help="device copy run before every timed decode-sweep call so that no "
                         "expert weight is served from the 256 MB MALL or the L2s")
@@ -347,6 +349,76 @@ def decode_sweep(args, weights):
             "points": out}
 
 
+def w4a16_leg(args, weights):
+    """The W4A16 mode (moe_layer_forward_w4a16: bf16 activations against the same resident
+    NVFP4 weights, the pages' GEMV arithmetic) on ragged570 and ragged2303, timed like the
+    main leg (graph replays after the settle), and on decode M = 1, 8, 32 like the M sweep
+    (cache flush before each call).  Also the largest difference between the W4A16 and
+    W4A4 layer outputs on ragged570, relative to the W4A16 row RMS (informational: two
+    different arithmetics, [GG] "Numbers")."""
+    import torch
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    res = {}
+    for name in ("ragged570", "ragged2303"):
+        wl = W.make_workload(name)
+        dl = L.DeviceLayer(wl, weights=weights, arithmetic="w4a16")
+        out16 = dl.forward().clone()
+        med, lo, hi, graph = time_graph(dl, args.steps, args.warmup, args.settle_ms)
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(dl.out, out16):
+            raise RuntimeError("W4A16 %s: graph replay differs from the eager output" % name)
+        n_act = len(wl.active_experts())
+        wbytes = n_act * LAYER_BYTES_PER_EXPERT
+        r = {"layer_ms_median": med, "layer_ms_min": lo, "layer_ms_max": hi,
+             "weight_GBps": wbytes / (med * 1e-3) / 1e9,
+             "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        if name == "ragged570":
+            d4 = L.DeviceLayer(wl, weights=weights)
+            o4 = d4.forward().view(torch.bfloat16).float()
+            o16 = out16.view(torch.bfloat16).float()
+            rms = o16.pow(2).mean(dim=1, keepdim=True).sqrt()
+            r["max_diff_vs_w4a4_over_row_rms"] = float(((o4 - o16).abs() / rms).max())
+            r["rms_diff_vs_w4a4_over_rms"] = float((o4 - o16).pow(2).mean().sqrt()
+                                                   / o16.pow(2).mean().sqrt())
+            del d4
+        res[name] = r
+        log(json.dumps({"w4a16": name, **r}))
+        del graph, dl
+    nbytes = args.flush_mb << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    pts = []
+    for M in (1, 8, 32):
+        wl = W.make_workload("decode%d" % M)
+        dl = L.DeviceLayer(wl, weights=weights, arithmetic="w4a16")
+        graph = dl.capture_graph()
+
+        def step():
+            dst.copy_(src)
+            graph.replay()
+
+        warm(step, args.warmup, args.settle_ms)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            dst.copy_(src)
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        med = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        n_act = len(wl.active_experts())
+        wbytes = n_act * LAYER_BYTES_PER_EXPERT
+        pts.append({"M": M, "layer_us": med * 1e3, "weight_GBps": wbytes / (med * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS})
+        log(json.dumps({"w4a16_decode": pts[-1]}))
+        del graph, dl
+    res["decode"] = pts
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -372,6 +444,10 @@ def main():
     if not args.no_decode_sweep and wl.E == 288:
         log("decode M sweep")
         sweep = decode_sweep(args, weights)
+    w4a16 = None
+    if not args.no_w4a16 and wl.E == 288:
+        log("W4A16 leg")
+        w4a16 = w4a16_leg(args, weights)
 
     # dominant kernel: the w13 grouped GEMM (one grouped_gemm_nvfp4 call)
     R, H, I = wl.R, wl.H, wl.I
@@ -405,6 +481,7 @@ def main():
         "frac_of_hbm_peak_eager": res["frac_of_hbm_peak_eager"],
         "w13_gemm_ms": res["w13_gemm_ms"], "w13_weight_GBps": res["w13_GBps"],
         "roofline": roofline, "cpu_baseline": cpu, "also": also, "decode_sweep": sweep,
+        "w4a16": w4a16,
         "host": platform.node(),
     }
     print(json.dumps(line), flush=True)

@@ -151,7 +151,7 @@ def _run_group(B, x, S, H, a_expert, a_src, a_dst, a_w, E, T):
 
 
 @pytest.mark.parametrize("case", ["random_invalid", "ragged570", "zipf", "empty", "one_expert",
-                                  "many_experts", "ragged2303", "large_uncached"])
+                                  "many_experts", "ragged2303", "large_uncached", "max_experts"])
 def test_group_gather_bit_exact(lib, case):
     from nvfp4_block_scaled_gather_amd import binding as B
     say("group", case)
@@ -180,6 +180,11 @@ def test_group_gather_bit_exact(lib, case):
     elif case == "many_experts":      # key ranges too wide for per-wave histograms
         E, S, T, R = 3000, 700, 50, 700
         a_expert = rng.integers(-1, E + 1, R)
+        a_src = np.arange(R)
+        a_dst = rng.integers(0, T, R)
+    elif case == "max_experts":       # E = 8192, the library's limit
+        E, S, T, R = 8192, 512, 64, 512
+        a_expert = rng.integers(0, E, R)
         a_src = np.arange(R)
         a_dst = rng.integers(0, T, R)
     elif case == "large_uncached":    # too many assignments to hold in LDS: global reads
@@ -315,6 +320,26 @@ def test_gemm_random_within_tolerance(lib, flags):
     rms = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True))
     err = np.abs(got - want)
     assert np.all(np.isfinite(got))
+    assert np.all(err <= GEMM_TOL * rms), float((err / rms).max())
+
+
+@pytest.mark.parametrize("flags", [0, 2])
+def test_gemm_largest_k_smallest_n(lib, flags):
+    """K = 8192 (64 chunks, eight scale groups) with N = 16 (a single tile per expert)."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm K=8192 N=16", flags)
+    rng = np.random.default_rng(110 + flags)
+    N, K = 16, 8192
+    sizes = [3, 0, 17]
+    E = len(sizes)
+    off = offsets_from_sizes(sizes)
+    aq, as_ = _workload_like(rng, int(off[-1]), K)
+    wn, wsc = rand_nvfp4(rng, E * N, K, 0x20, 0x40)
+    wp = pack(B, wn, wsc, E, N, K)
+    got = run_gemm(B, aq, as_, off, wp, N, K, flags, gemv_max=0)
+    want = _oracle_gemm(aq, as_, off, wn, wsc, E, N, K)
+    rms = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True))
+    err = np.abs(got - want)
     assert np.all(err <= GEMM_TOL * rms), float((err / rms).max())
 
 

@@ -174,6 +174,48 @@ def test_layer_drops_invalid_assignments(lib):
     assert clean.device_error() == 0
 
 
+@pytest.mark.parametrize("arithmetic", ["w4a4", "w4a16"])
+def test_layer_empty_batch_and_tokens_without_rows(lib, arithmetic):
+    """No assignments at all: every output row is zero and no error is raised.  Tokens
+    that no assignment routes to come out zero while the others are unchanged."""
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("empty batch / idle tokens", arithmetic)
+    wl = W.make_workload("tiny")
+    base = L.DeviceLayer(wl, arithmetic=arithmetic)
+    want = host(base.forward()).copy()
+    empty_wl = W.Workload(**{**wl.__dict__, "a_expert": np.zeros(0, np.int32),
+                             "a_src": np.zeros(0, np.int32), "a_dst": np.zeros(0, np.int32),
+                             "a_w": np.zeros(0, np.float32)})
+    d0 = L.DeviceLayer(empty_wl, weights=(base.w13, base.w2), arithmetic=arithmetic)
+    got0 = host(d0.forward())
+    assert d0.device_error() == 0
+    assert not got0.any()
+    wide = W.Workload(**{**wl.__dict__, "T": wl.T + 3})       # three tokens with no rows
+    d1 = L.DeviceLayer(wide, weights=(base.w13, base.w2), arithmetic=arithmetic)
+    got1 = host(d1.forward())
+    assert d1.device_error() == 0
+    assert np.array_equal(got1[:wl.T], want)
+    assert not got1[wl.T:].any()
+
+
+def test_layer_at_the_largest_hidden_size(lib):
+    """H = 8192, the largest the row kernels and the layer accept: the w13 GEMM stages
+    16 rows of 4.5 KiB (more than 64 KiB of LDS) and w2 has N = 8192."""
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("layer H=8192")
+    wl = W.make_workload("ragged570", E=6, H=8192, I=256)
+    dl = L.DeviceLayer(wl)
+    got = host(dl.forward()).view(np.uint16).copy()
+    assert dl.device_error() == 0
+    want = omoe.layer_forward(wl.x, wl.a_expert, wl.a_src, wl.a_dst, wl.a_w, wl.T, wl.w13, wl.w2,
+                              wl.g_gate, wl.g_up, wl.g_down, wl.E, wl.H, wl.I)
+    frac, worst = _e2e_ok(got, want)
+    say("H=8192: fraction within tolerance %.5f, worst %.4f x RMS" % (frac, worst))
+    assert frac >= E2E_FRAC
+
+
 # ------------------------------------------------------------------------------ full size
 @pytest.fixture(scope="module")
 def full_weights():

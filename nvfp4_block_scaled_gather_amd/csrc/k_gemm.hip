@@ -84,10 +84,9 @@ struct GemmArgs {
 };
 
 // ------------------------------------------------------------------------- LDS layout
-// [E x uint16 active-expert list, padded to 16 B][rows x q_stride nibbles][rows x s_stride
-// scales].  The row strides are padded so that the 16 rows a wave reads at once fall in
+// [rows x q_stride nibbles][rows x s_stride scales] (or [rows x b_stride bf16]).  The row
+// strides are padded so that the 16 rows a wave reads at once fall in
 // distinct banks (a nibble row stride of 16 mod 256 bytes, a scale row stride of 8 mod 256).
-__host__ __device__ __forceinline__ int act_list_bytes(int E) { return (2 * E + 15) & ~15; }
 __host__ __device__ __forceinline__ int q_stride(int K) { return K / 2 + 16; }
 __host__ __device__ __forceinline__ int s_stride(int K) { return K / 16 + 8; }
 // bf16 activation rows (W4A16): 2K bytes, padded the same way.
@@ -96,39 +95,62 @@ __host__ __device__ __forceinline__ int b_stride(int K) { return 2 * K + 16; }
 // columns plus padding), which for small K is larger than the staged rows; 256 bytes of
 // slack keep the B-operand prefetch past the last chunk inside the allocation.
 static size_t out_block_bytes(int NS, int waves) { return (size_t)kPassRows * (16 * NS * waves + 4) * 4; }
-static size_t gemm_lds_bytes(int E, int K, int rows, bool abf = false, int NS = 2,
+static size_t gemm_lds_bytes(int K, int rows, bool abf = false, int NS = 2,
                              int waves = kGemmWaves) {
   const size_t stage = (size_t)rows * (abf ? b_stride(K) : q_stride(K) + s_stride(K));
   const size_t outb = out_block_bytes(NS, waves);
-  return (size_t)act_list_bytes(E) + (stage > outb ? stage : outb) + 256;
+  return (stage > outb ? stage : outb) + 256;
 }
 
-// Ids of the experts whose group size is in [gmin, gmax], ascending, into LDS (wave 0).
-__device__ __forceinline__ int build_active_list(const GemmArgs& p, uint16_t* s_act, int* s_nact) {
+// The group of a workgroup's item.  Active groups are the experts whose group size is in
+// [gmin, gmax], in ascending expert id; item it of a launch belongs to active group
+// it / items_per_e.  Wave 0 scans the offsets (512 experts per round, all loads of a round
+// in flight together) until it has counted past group ai, and the lane that holds it
+// publishes (expert, first row, size) through LDS.  Returns false if there are at most ai
+// active groups (the workgroup has no item).
+struct ItemGroup {
+  int e, r0, G;
+};
+
+__device__ __forceinline__ bool find_group(const GemmArgs& p, int ai, int* s_grp, ItemGroup& g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     int n = 0;
-    for (int base = 0; base < p.E; base += 256) {
-      int g[4];
+    bool found = false;
+    for (int base = 0; base < p.E && !found; base += 512) {  // uniform
+      int lo[8], hi[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {  // four independent loads in flight
+      for (int u = 0; u < 8; ++u) {
         const int e = base + 64 * u + lane;
-        g[u] = e < p.E ? p.off[e + 1] - p.off[e] : 0;
+        lo[u] = e < p.E ? p.off[e] : 0;
+        hi[u] = e < p.E ? p.off[e + 1] : 0;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int e = base + 64 * u + lane;
-        const bool a = e < p.E && g[u] >= p.gmin && g[u] <= p.gmax;
+        const int sz = hi[u] - lo[u];
+        const bool a = e < p.E && sz >= p.gmin && sz <= p.gmax;
         const uint64_t m = __ballot(a);
-        if (a) s_act[n + __popcll(m & below)] = (uint16_t)e;
-        n += __popcll(m);
+        const int c = __popcll(m);
+        if (!found && ai < n + c) {  // uniform
+          if (a && n + __popcll(m & below) == ai) {
+            s_grp[0] = e;
+            s_grp[1] = lo[u];
+            s_grp[2] = sz;
+          }
+          found = true;
+        }
+        n += c;
       }
     }
-    if (lane == 0) *s_nact = n;
+    if (lane == 0) s_grp[3] = found ? 1 : 0;
   }
   __syncthreads();
-  return __builtin_amdgcn_readfirstlane(*s_nact);
+  g.e = __builtin_amdgcn_readfirstlane(s_grp[0]);
+  g.r0 = __builtin_amdgcn_readfirstlane(s_grp[1]);
+  g.G = __builtin_amdgcn_readfirstlane(s_grp[2]);
+  return __builtin_amdgcn_readfirstlane(s_grp[3]) != 0;
 }
 
 // Buffer resource over [base, base + bytes): loads at offsets beyond the range return 0
@@ -426,55 +448,34 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   }
 }
 
-// Item -> (expert, first tile of this wave).
-struct ItemLoop {
-  int items_per_e, total, tiles, per_item;
-};
-
-__device__ __forceinline__ ItemLoop item_loop(const GemmArgs& p, int nact, int NS, int waves) {
-  ItemLoop L;
-  L.tiles = p.N / 16;
-  L.per_item = waves * NS;
-  L.items_per_e = (L.tiles + L.per_item - 1) / L.per_item;
-  L.total = nact * L.items_per_e;
-  return L;
-}
-
-template <int NS, int D, int S, bool SWI, bool ABF, int WAVES>
+// One workgroup per item: item it covers tiles [ii * per_item, (ii + 1) * per_item) of active
+// group it / items_per_e (ii = it % items_per_e).  The grid has one item slot per group
+// that can be non-empty, so every item has a workgroup and no workgroup has two.
+// PR: activation rows staged per pass (at most the B operand's 16 columns).
+template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, int PR>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_nact;
-  uint16_t* s_act = (uint16_t*)smem;
-  const int nact = build_active_list(p, s_act, &s_nact);
-  uint8_t* s_q = smem + act_list_bytes(p.E);
-  uint8_t* s_s = s_q + kPassRows * q_stride(p.K);  // NVFP4 scales (unused with ABF)
+  __shared__ int s_grp[4];
+  uint8_t* s_q = smem;
+  uint8_t* s_s = s_q + PR * q_stride(p.K);  // NVFP4 scales (unused with ABF)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // SWI: a wave owns one gate tile (and the matching up tile)
-  ItemLoop L;
-  if (SWI) {
-    L.tiles = p.I / 16;
-    L.per_item = WAVES;
-    L.items_per_e = (L.tiles + L.per_item - 1) / L.per_item;
-    L.total = nact * L.items_per_e;
-  } else {
-    L = item_loop(p, nact, NS, WAVES);
-  }
+  const int tiles = SWI ? p.I / 16 : p.N / 16;
+  const int per_item = SWI ? WAVES : WAVES * NS;
+  const int items_per_e = (tiles + per_item - 1) / per_item;
+  ItemGroup g;
+  if (!find_group(p, blockIdx.x / items_per_e, s_grp, g)) return;  // uniform
+  const int t0 = (blockIdx.x % items_per_e) * per_item + wave * (SWI ? 1 : NS);
+  const int nsv = SWI ? (t0 < tiles ? 2 : 0) : min(NS, tiles - t0);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
-  for (int it = blockIdx.x; it < L.total; it += gridDim.x) {  // uniform over the workgroup
-    const int e = __builtin_amdgcn_readfirstlane(s_act[it / L.items_per_e]);
-    const int t0 = (it % L.items_per_e) * L.per_item + wave * (SWI ? 1 : NS);
-    const int nsv = SWI ? (t0 < L.tiles ? 2 : 0) : min(NS, L.tiles - t0);
-    const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
-    const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
-    const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
-    const float ggate = SWI ? p.g_gate[e] : p.c_w ? p.c_g[e] : 0.f;
-    const float gup = SWI ? p.g_up[e] : 0.f;
-    for (int b = 0; b < G; b += kPassRows) {
-      __syncthreads();  // the previous pass is done with the staged rows
-      mfma_pass<NS, D, S, SWI, ABF, WAVES>(p, wt, nsv, r0 + b, min(kPassRows, G - b), 16 * t0,
-                                           s_q, s_s, ggate, gup);
-    }
+  const uint8_t* wt = p.w + (size_t)g.e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+  const float ggate = SWI ? p.g_gate[g.e] : p.c_w ? p.c_g[g.e] : 0.f;
+  const float gup = SWI ? p.g_up[g.e] : 0.f;
+  for (int b = 0; b < g.G; b += PR) {
+    if (b) __syncthreads();  // the previous pass is done with the staged rows
+    mfma_pass<NS, D, S, SWI, ABF, WAVES>(p, wt, nsv, g.r0 + b, min(PR, g.G - b), 16 * t0,
+                                         s_q, s_s, ggate, gup);
   }
 }
 
@@ -556,35 +557,30 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
 template <int NS, int D, int S>
 __global__ __launch_bounds__(256) void k_gemm_gemv(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_nact;
-  uint16_t* s_act = (uint16_t*)smem;
-  const int nact = build_active_list(p, s_act, &s_nact);
-  uint8_t* s_q = smem + act_list_bytes(p.E);
+  __shared__ int s_grp[4];
+  uint8_t* s_q = smem;
   uint8_t* s_s = s_q + kGemvRows * q_stride(p.K);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const ItemLoop L = item_loop(p, nact, NS, kGemmWaves);
+  const int tiles = p.N / 16, per_item = kGemmWaves * NS;
+  const int items_per_e = (tiles + per_item - 1) / per_item;
+  ItemGroup g;
+  if (!find_group(p, blockIdx.x / items_per_e, s_grp, g)) return;  // uniform
+  const int t0 = (blockIdx.x % items_per_e) * per_item + wave * NS;
+  const int nsv = min(NS, tiles - t0);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
-  for (int it = blockIdx.x; it < L.total; it += gridDim.x) {
-    const int e = __builtin_amdgcn_readfirstlane(s_act[it / L.items_per_e]);
-    const int t0 = (it % L.items_per_e) * L.per_item + wave * NS;
-    const int nsv = min(NS, L.tiles - t0);
-    const int r0 = __builtin_amdgcn_readfirstlane(p.off[e]);
-    const int G = __builtin_amdgcn_readfirstlane(p.off[e + 1]) - r0;
-    const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
-    const float gdown = p.c_w ? p.c_g[e] : 0.f;
-    for (int b = 0; b < G; b += kGemvRows) {
-      __syncthreads();
-      gemv_pass<NS, D, S>(p, wt, nsv, r0 + b, min(kGemvRows, G - b), 16 * t0, s_q, s_s, gdown);
-    }
+  const uint8_t* wt = p.w + (size_t)g.e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+  const float gdown = p.c_w ? p.c_g[g.e] : 0.f;
+  for (int b = 0; b < g.G; b += kGemvRows) {
+    if (b) __syncthreads();
+    gemv_pass<NS, D, S>(p, wt, nsv, g.r0 + b, min(kGemvRows, g.G - b), 16 * t0, s_q, s_s, gdown);
   }
 }
 
 // ------------------------------------------------------------------------- launch
 // Grid: one workgroup per item that can have work.  At most min(E, R) groups are non-empty
 // (R grouped rows), so the grid is min(E, R) x items per expert; workgroups past the active
-// items exit after building the active list, and a workgroup loops over items if the grid
-// is smaller than their count.
+// items exit once they have scanned the offsets.
 static int items_per_expert(int per_item, const GemmArgs& a) {
   return (a.N / 16 + per_item - 1) / per_item;
 }
@@ -615,15 +611,16 @@ static hipError_t launch_one(Kern kern, int per_item, const GemmArgs& a, size_t 
 
 // The packed layout's scale group S fixes the kernel instance; the ring depth D is capped
 // at S.
-template <int NS, int D, bool SWI, bool ABF = false, int WAVES = kGemmWaves>
+template <int NS, int D, bool SWI, bool ABF = false, int WAVES = kGemmWaves, int PR = kPassRows>
 static hipError_t launch_mfma_t(const GemmArgs& a, int per, int R, hipStream_t s) {
-  const size_t lds = gemm_lds_bytes(a.E, a.K, kPassRows, ABF, NS, WAVES);
+  static_assert(PR >= 1 && PR <= kPassRows, "a pass feeds at most the B operand's 16 columns");
+  const size_t lds = gemm_lds_bytes(a.K, PR, ABF, NS, WAVES);
   const int th = 64 * WAVES;
   switch (scale_group(a.K / 128)) {
-    case 8: return launch_one(k_gemm_mfma<NS, (D < 8 ? D : 8), 8, SWI, ABF, WAVES>, per, a, lds, th, R, s);
-    case 4: return launch_one(k_gemm_mfma<NS, (D < 4 ? D : 4), 4, SWI, ABF, WAVES>, per, a, lds, th, R, s);
-    case 2: return launch_one(k_gemm_mfma<NS, (D < 2 ? D : 2), 2, SWI, ABF, WAVES>, per, a, lds, th, R, s);
-    default: return launch_one(k_gemm_mfma<NS, 1, 1, SWI, ABF, WAVES>, per, a, lds, th, R, s);
+    case 8: return launch_one(k_gemm_mfma<NS, (D < 8 ? D : 8), 8, SWI, ABF, WAVES, PR>, per, a, lds, th, R, s);
+    case 4: return launch_one(k_gemm_mfma<NS, (D < 4 ? D : 4), 4, SWI, ABF, WAVES, PR>, per, a, lds, th, R, s);
+    case 2: return launch_one(k_gemm_mfma<NS, (D < 2 ? D : 2), 2, SWI, ABF, WAVES, PR>, per, a, lds, th, R, s);
+    default: return launch_one(k_gemm_mfma<NS, 1, 1, SWI, ABF, WAVES, PR>, per, a, lds, th, R, s);
   }
 }
 
@@ -639,7 +636,7 @@ static hipError_t launch_mfma(const GemmArgs& a, int R, hipStream_t s) {
 static hipError_t launch_gemv(const GemmArgs& a, int R, hipStream_t s) {
   const int per = kGemmWaves * MOE_GEMV_NS;
   constexpr int D = MOE_GEMV_D;
-  const size_t lds = gemm_lds_bytes(a.E, a.K, kGemvRows);
+  const size_t lds = gemm_lds_bytes(a.K, kGemvRows);
   switch (scale_group(a.K / 128)) {
     case 8: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 8 ? D : 8), 8>, per, a, lds, 256, R, s);
     case 4: return launch_one(k_gemm_gemv<MOE_GEMV_NS, (D < 4 ? D : 4), 4>, per, a, lds, 256, R, s);
@@ -699,6 +696,15 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
 // for one workgroup per CU, so the W4A16 instances run 16 waves per workgroup: the same 16
 // waves per CU stream weights against one shared copy of the staged rows.
 constexpr int kW4A16Waves = 16;
+// A small batch would leave most CUs idle with such workgroups (at one row per group, 8
+// items per expert at N = 4096), so it runs the small-grid shape of the NVFP4 instances
+// (4 waves, deep ring) staging 4 rows per pass: 32 KiB at K = 4096, four workgroups per
+// CU.  It is taken only when there are at most as many rows as experts, so that passes of
+// 4 rows rarely repeat a group's weight stream (a decode step of up to 4 tokens, top-k,
+// never does: no group has more rows than tokens).
+constexpr int kSmallW4A16PassRows = 4;
+
+static bool small_w4a16(const GemmArgs& a, int R) { return small_grid(a, R) && R <= a.E; }
 
 hipError_t launch_grouped_gemm_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
                                      const int32_t* off, int E, int R, const uint8_t* w, int N,
@@ -708,6 +714,8 @@ hipError_t launch_grouped_gemm_w4a16(const uint16_t* ab, const int32_t* amap, in
   a.c_w = c_w;
   a.c_g = c_g;
   a.ab = ab;
+  if (small_w4a16(a, R))
+    return launch_mfma_t<1, 8, false, true, kGemmWaves, kSmallW4A16PassRows>(a, kGemmWaves, R, s);
   return launch_mfma_t<2, MOE_GEMM_D, false, true, kW4A16Waves>(a, 2 * kW4A16Waves, R, s);
 }
 
@@ -718,7 +726,10 @@ hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* a
   GemmArgs a{nullptr, nullptr, amap, a_rows, off, E, w13, 2 * I, K, nullptr, 1, 0x7FFFFFFF,
              g_gate, g_up, nullptr, nullptr, h, I};
   a.ab = ab;
-  // one gate tile per wave: (I/16)/16 items per expert, the grid of N = 2I with 32 per item
+  // one gate tile per wave: (I/WAVES)/16 items per expert, the grid of N = 2I with 2 WAVES
+  // tiles per item
+  if (small_w4a16(a, R))
+    return launch_mfma_t<2, 8, true, true, kGemmWaves, kSmallW4A16PassRows>(a, 2 * kGemmWaves, R, s);
   return launch_mfma_t<2, MOE_GEMM_D, true, true, kW4A16Waves>(a, 2 * kW4A16Waves, R, s);
 }
 

@@ -127,6 +127,33 @@ def test_w4a16_gemm_row_invariance_and_determinism(lib):
         assert np.array_equal(r.view(np.uint32), again[0].view(np.uint32))
 
 
+def test_w4a16_gemm_small_batch_instance_agrees_bitwise(lib):
+    """A batch with no more rows than experts runs the small-batch instance (4 waves, 4 rows
+    staged per pass: a group of 13 rows takes passes of 4, 4, 4 and 1 rows); the same rows
+    in a larger batch run the 16-wave instance.  Both give the same bits (the instance
+    changes which wave computes an output and how far ahead it loads, never the order of
+    its accumulation), and both stay within tolerance of the oracle."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("w4a16 small-batch instance")
+    rng = np.random.default_rng(98)
+    E, N, K = 64, 256, 1024
+    wn, wsc, wp = _weights(B, rng, E, N, K)
+    big_sizes = np.full(E, 2)
+    big_sizes[5], big_sizes[40] = 13, 1
+    big_off = offsets_from_sizes(big_sizes)
+    a = _bf16(rng.standard_normal((int(big_off[-1]), K)))
+    big = run_w4a16(B, a, big_off, wp, N, K)            # 138 rows > 64 experts
+    small_sizes = np.zeros(E, np.int64)
+    small_sizes[5], small_sizes[40] = 13, 1
+    rows = np.concatenate([np.arange(big_off[5], big_off[6]), np.arange(big_off[40], big_off[41])])
+    small_off = offsets_from_sizes(small_sizes)
+    small = run_w4a16(B, a[rows], small_off, wp, N, K)  # 14 rows <= 64 experts
+    assert np.array_equal(small.view(np.uint32), big[rows].view(np.uint32))
+    want = _oracle(a[rows], small_off, wn, wsc, N, K)
+    rms = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True))
+    assert np.all(np.abs(small - want) <= GEMM_TOL * rms)
+
+
 def _out_f64(bits):
     return onv.bf16_bits_to_f32(np.asarray(bits).view(np.uint16)).astype(np.float64)
 

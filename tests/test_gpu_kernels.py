@@ -151,8 +151,12 @@ def _run_group(B, x, S, H, a_expert, a_src, a_dst, a_w, E, T):
 
 
 @pytest.mark.parametrize("case", ["random_invalid", "ragged570", "zipf", "empty", "one_expert",
-                                  "many_experts", "ragged2303", "large_uncached", "max_experts"])
+                                  "many_experts", "ragged2303", "large_uncached", "max_experts",
+                                  "small_invalid", "small_decode4", "small_one_row",
+                                  "small_wide_keys", "small_one_expert", "small_33"])
 def test_group_gather_bit_exact(lib, case):
+    """Grouping and gather bit-exact against the oracle.  The "small_" cases have at most 32
+    assignments (the one-wave grouping; "small_33" is the first size past it)."""
     from nvfp4_block_scaled_gather_amd import binding as B
     say("group", case)
     rng = np.random.default_rng(sum(map(ord, case)))
@@ -191,6 +195,32 @@ def test_group_gather_bit_exact(lib, case):
         E, S, T, R = 64, 40000, 500, 40000
         a_expert = rng.integers(-1, E, R)
         a_src = np.arange(R)
+        a_dst = rng.integers(0, T, R)
+    elif case == "small_invalid":
+        E, S, T, R = 13, 20, 9, 30
+        a_expert = rng.integers(-2, E + 2, R)
+        a_src = rng.integers(-1, S + 1, R)
+        a_dst = rng.integers(-1, T + 1, R)
+    elif case in ("small_decode4", "small_33"):   # top-8 of 288 for 4 tokens: R = 32
+        E, T = 288, 4
+        a_expert = np.concatenate([rng.choice(E, 8, replace=False) for _ in range(T)])
+        a_src = np.repeat(np.arange(T), 8)
+        a_dst = a_src.copy()
+        if case == "small_33":
+            a_expert, a_src, a_dst = (np.append(v, v[:1]) for v in (a_expert, a_src, a_dst))
+        S, R = T, len(a_expert)
+    elif case == "small_one_row":
+        E, S, T, R = 288, 1, 1, 1
+        a_expert, a_src, a_dst = np.array([287]), np.array([0]), np.array([0])
+    elif case == "small_wide_keys":   # E and T far above 64: many offsets per lane
+        E, S, T, R = 8192, 32, 5000, 32
+        a_expert = rng.integers(-1, E, R)
+        a_src = np.arange(R)
+        a_dst = rng.integers(0, T, R)
+    elif case == "small_one_expert":  # 32 equal keys: order by assignment index
+        E, S, T, R = 6, 10, 3, 32
+        a_expert = np.full(R, 5)
+        a_src = rng.integers(0, S, R)
         a_dst = rng.integers(0, T, R)
     elif case == "ragged2303":
         E, S, T, R = 288, 2303, 288, 2303

@@ -703,6 +703,7 @@ constexpr int kW4A16Waves = 16;
 // 4 rows rarely repeat a group's weight stream (a decode step of up to 4 tokens, top-k,
 // never does: no group has more rows than tokens).
 constexpr int kSmallW4A16PassRows = 4;
+constexpr int kW4A16PassRows8 = 8;
 
 static bool small_w4a16(const GemmArgs& a, int R) { return small_grid(a, R) && R <= a.E; }
 
@@ -734,6 +735,11 @@ hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* a
   // tiles per item
   if (small_w4a16(a, R))
     return launch_mfma_t<2, 8, true, true, kGemmWaves, kSmallW4A16PassRows>(a, 2 * kGemmWaves, R, s);
+  // At most 4 rows per expert on average, groups rarely exceed 8 rows: staging 8 rows per
+  // pass (64 KiB at K = 4096) fits two 8-wave workgroups per CU (the W4A16 layer measured
+  // 3.7% faster on ragged570 than with one 16-wave workgroup staging 16 rows).
+  if (R <= 4 * E)
+    return launch_mfma_t<2, MOE_GEMM_D, true, true, 8, kW4A16PassRows8>(a, 2 * 8, R, s);
   return launch_mfma_t<2, MOE_GEMM_D, true, true, kW4A16Waves>(a, 2 * kW4A16Waves, R, s);
 }
 

@@ -209,3 +209,32 @@ def test_w4a16_layer_batch_parity_and_graph_replay(lib):
         assert np.array_equal(alone[t], full[t]), t
     del g
     torch.cuda.synchronize()
+
+
+def test_w4a16_layer_eight_row_passes(lib):
+    """A batch of at most 4 rows per expert on average and groups above 8 rows: the w13 GEMM
+    runs 8-wave workgroups staging 8 rows per pass, so the large groups take several
+    passes.  The layer stays within the end-to-end bar of the oracle, and a token computed
+    alone (on the small-batch instances) has the same bits as in the batch."""
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("w4a16 eight-row passes")
+    wl = W.make_workload("zipf512", E=160, H=256, I=256)
+    assert wl.R <= 4 * wl.E and np.bincount(wl.a_expert, minlength=wl.E).max() > 8
+    dl = L.DeviceLayer(wl, arithmetic="w4a16")
+    full = host(dl.forward()).view(np.uint16).copy()
+    assert dl.device_error() == 0
+    want = omoe.layer_forward_w4a16(wl.x, wl.a_expert, wl.a_src, wl.a_dst, wl.a_w, wl.T, wl.w13,
+                                    wl.w2, wl.g_gate, wl.g_up, wl.g_down, wl.E, wl.H, wl.I)
+    frac, worst = _e2e_ok(full, want)
+    say("fraction within tolerance %.5f, worst %.4f x RMS" % (frac, worst))
+    assert frac >= E2E_FRAC
+    hot = int(np.argmax(np.bincount(wl.a_expert, minlength=wl.E)))
+    for t in sorted(set(wl.a_dst[wl.a_expert == hot].tolist()))[:2]:
+        sel = np.where(wl.a_dst == t)[0]
+        one = W.Workload(**{**wl.__dict__, "a_expert": wl.a_expert[sel], "a_src": wl.a_src[sel],
+                            "a_dst": wl.a_dst[sel], "a_w": wl.a_w[sel]})
+        d1 = L.DeviceLayer(one, weights=(dl.w13, dl.w2), arithmetic="w4a16")
+        alone = host(d1.forward()).view(np.uint16)
+        sync()
+        assert np.array_equal(alone[t], full[t]), t

@@ -14,7 +14,9 @@ work after the GPU was idle).
 Metric (the pages' own byte model, table "Bytes decide it before the kernel runs" of the
 [MF]): weight-stream GB/s = active experts x 14,155,776 B / layer time.
 
-Prints ONE JSON line.  Also times the dominant kernel (the w13 grouped GEMM) with HIP
+Prints ONE JSON line.  The workloads in --also (default: ragged2303 and the skewed zipf512
+decode batch) are timed the same way in the same run.  Also times the dominant kernel (the
+w13 grouped GEMM) with HIP
 events on its own stream over a loop of launches on the layer's real inputs, and the CPU
 oracle on a bounded sample of the same workload (cpu_baseline).
 
@@ -62,8 +64,9 @@ def parse():
     p.add_argument("--flush-mb", type=int, default=512,
                    help="device copy run before every timed decode-sweep call so that no "
                         "expert weight is served from the 256 MB MALL or the L2s")
-    p.add_argument("--also", default="ragged2303",
-                   help="second workload timed in the same run ('' for none)")
+    p.add_argument("--also", default="ragged2303,zipf512",
+                   help="comma-separated workloads timed in the same run after the main one "
+                        "('' for none)")
     p.add_argument("--flags", type=int, default=None, help="GEMM path (0 auto, 1 GEMV, 2 MFMA)")
     p.add_argument("--gemv-max-rows", type=int, default=None)
     p.add_argument("--kernel-iters", type=int, default=30)
@@ -436,9 +439,11 @@ def main():
     B.load()
     wl, dl, res, weights = run_workload(args.workload, args)
     also = {}
-    if args.also and args.also != args.workload and wl.E == 288:
-        _, dl2, res2, _ = run_workload(args.also, args, weights)
-        also[args.also] = res2
+    for name in (n for n in args.also.split(",") if n and n != args.workload):
+        if wl.E != 288:
+            break
+        _, dl2, res2, _ = run_workload(name, args, weights)
+        also[name] = res2
         del dl2
     sweep = None
     if not args.no_decode_sweep and wl.E == 288:

@@ -719,9 +719,10 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
 }
 
 // ------------------------------------------------------------------------- W4A16
-// bf16 activations (2K bytes per staged row: 128 KiB for 16 rows at K = 4096) leave room
-// for one workgroup per CU, so the W4A16 instances run 16 waves per workgroup: the same 16
-// waves per CU stream weights against one shared copy of the staged rows.
+// bf16 activations take 2K bytes per staged row (128 KiB for 16 rows at K = 4096), which
+// leaves room for one workgroup per CU: the general W4A16 instance runs 16 waves per
+// workgroup, the same 16 waves per CU streaming weights against one shared copy of the
+// staged rows.  Batch shapes that allow it take smaller workgroups (below).
 constexpr int kW4A16Waves = 16;
 // A small batch would leave most CUs idle with such workgroups (at one row per group, 8
 // items per expert at N = 4096), so it runs the small-grid shape of the NVFP4 instances

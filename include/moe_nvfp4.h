@@ -218,9 +218,11 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
  * one stream, with no host synchronization ([GG], section "What changed").
  * The S source rows are quantized once each, in the same launch as the grouping, and the
  * w13 GEMM reads grouped row i from source row row_src[i] (a row's codes depend only on
- * the row, so this equals gather-then-quantize); the second quantize is fused into
- * SwiGLU.  The results are bit-identical to calling the separate entry points in
- * sequence.
+ * the row, so this equals gather-then-quantize).  When every group runs on the MFMA path
+ * (the default), SwiGLU runs in the w13 GEMM's epilogue and h is quantized by one small
+ * launch; with GEMV groups, SwiGLU and the second quantization are one kernel.  The w2 GEMM
+ * writes each row's weighted scatter term, summed per token by the last launch.  The
+ * results are bit-identical to calling the separate entry points in sequence.
  *
  * L (host): E, H, I; w13_packed (E x [2I, H], gate rows first) and w2_packed
  *   (E x [H, I]) from nvfp4_pack_weights; per-expert globals g_gate, g_up, g_down [E];

@@ -165,3 +165,21 @@ def test_bf16_rounding_float64_ties_and_double_rounding():
     assert nvfp4.f64_to_bf16_bits(0.0) == 0x0000
     assert nvfp4.f64_to_bf16_bits(3.4e38) == 0x7F80        # above max: overflows to inf
     assert nvfp4.f64_to_bf16_bits(2.0 ** -133) == 0x0001   # smallest subnormal
+
+
+def test_every_element_scale_product_is_exact_in_bf16_and_every_pair_in_fp32():
+    """The exactness the GEMMs rely on: an e2m1 value times an e4m3fn scale has at most
+    2 + 4 significant bits and stays inside bf16's exponent range, so every such product
+    (all 16 element codes x all 254 finite scale codes) is a bf16 value; and the product
+    of two of them has at most 12 significant bits, so it is exact in fp32.  Checked by
+    rounding each product to bf16 / fp32 and comparing with the float64 value."""
+    e2 = nvfp4.e2m1_decode(np.arange(16))
+    s8 = nvfp4.e4m3_decode(np.array([b for b in range(256) if b not in (0x7F, 0xFF)]))
+    assert len(s8) == 254 and np.isfinite(s8).all()
+    prods = np.unique(np.outer(e2, s8).ravel())
+    back = nvfp4.bf16_bits_to_f32(nvfp4.f64_to_bf16_bits(prods)).astype(np.float64)
+    assert np.array_equal(back, prods)
+    mags = np.unique(np.abs(prods[prods != 0]))
+    pairs = np.outer(mags, mags)                  # exact in float64 (<= 12 significant bits)
+    assert np.array_equal(pairs.astype(np.float32).astype(np.float64), pairs)
+    assert pairs.min() > 0 and pairs.max() < np.finfo(np.float32).max

@@ -121,3 +121,48 @@ def test_rows_are_independent():
     for i in range(5):
         qi, si, gi = nvfp4.quantize_row(X[i])
         assert np.array_equal(q[i], qi) and np.array_equal(s[i], si) and g[i] == gi
+
+
+def _exhaustive_nearest(v, table):
+    """Index of the value of `table` (ascending magnitudes, code = index) nearest to |v|
+    by exact rational comparison, ties to the even index, saturating at the last entry."""
+    from fractions import Fraction
+    a = abs(Fraction(float(v)))
+    best, best_d = 0, None
+    for i, t in enumerate(table):
+        d = abs(Fraction(float(t)) - a)
+        if best_d is None or d < best_d or (d == best_d and i % 2 == 0):
+            best, best_d = i, d
+    return best
+
+
+@pytest.mark.parametrize("rows", [1, 130])
+def test_quantizer_against_exhaustive_search(rows):
+    """The page's test shape (K = 64, one row and 130 rows of random values spanning many
+    binades): every scale byte and every element code equals the one found by searching
+    the whole e4m3 / e2m1 code tables with exact rational distances, applied to the
+    float32 quotients of the stated formulas."""
+    rng = np.random.default_rng(64 + rows)
+    x = (rng.standard_normal((rows, 64)) * np.exp2(rng.integers(-20, 20, (rows, 1)))).astype(np.float32)
+    x[0, 5] = -0.0
+    e2_pos = nvfp4.e2m1_decode(np.arange(8))
+    e4_pos = nvfp4.e4m3_decode(np.arange(0x7F))
+    for r in range(rows):
+        nib, sc, gs = nvfp4.quantize_row(x[r])
+        codes = nvfp4.unpack_nibbles(nib)
+        amax = np.float32(np.max(np.abs(x[r])))
+        assert gs == (np.float32(amax / np.float32(2688.0)) if amax > 0 else np.float32(1.0))
+        for b in range(4):
+            blk = x[r, 16 * b:16 * (b + 1)]
+            sf = np.float32(np.max(np.abs(blk)) / np.float32(np.float32(6.0) * gs))
+            want_sc = _exhaustive_nearest(sf, e4_pos)
+            assert sc[b] == want_sc, (r, b)
+            d = np.float32(np.float32(e4_pos[want_sc]) * gs)
+            for k in range(16):
+                got = int(codes[16 * b + k])
+                if d == 0:
+                    assert got == 0
+                    continue
+                q = np.float32(blk[k] / d)
+                want = _exhaustive_nearest(q, e2_pos) | (8 if np.signbit(q) else 0)
+                assert got == want, (r, b, k, float(q))

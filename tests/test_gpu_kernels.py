@@ -353,6 +353,37 @@ def test_gemm_random_within_tolerance(lib, flags):
     assert np.all(err <= GEMM_TOL * rms), float((err / rms).max())
 
 
+@pytest.mark.parametrize("flags", [1, 2])
+@pytest.mark.parametrize("K", [384, 640, 1152, 1536])
+def test_gemm_ragged_tiles_and_odd_scale_groups(lib, flags, K):
+    """N = 208 (13 tiles: one whole 8-tile item and a partial one per expert) and K with
+    3, 5, 9 or 12 chunks (scale groups of 1, 1, 1 and 4 chunks, rings of 1 to 4): random
+    GEMMs within tolerance of the oracle, and a row alone equals the row in its group."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("gemm ragged tiles K", K, "flags", flags)
+    rng = np.random.default_rng(K + flags)
+    N = 208
+    sizes = [1, 7, 0, 20]
+    E = len(sizes)
+    offsets = offsets_from_sizes(sizes)
+    R = int(offsets[-1])
+    aq, as_ = _workload_like(rng, R, K)
+    ws_ = [W.expert_weights(91, e, 0, N, K) for e in range(E)]
+    wn = np.concatenate([w[0] for w in ws_])
+    wsc = np.concatenate([w[1] for w in ws_])
+    wp = pack(B, wn, wsc, E, N, K)
+    got = run_gemm(B, aq, as_, offsets, wp, N, K, flags)
+    want = _oracle_gemm(aq, as_, offsets, wn, wsc, E, N, K)
+    rms = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True))
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - want) <= GEMM_TOL * rms), float((np.abs(got - want) / rms).max())
+    r = int(offsets[3]) + 13                       # a row of the 20-row group, alone
+    alone_off = offsets_from_sizes([0, 0, 0, 1])
+    alone = run_gemm(B, aq[r:r + 1], as_[r:r + 1], alone_off, wp, N, K, flags)
+    assert np.array_equal(alone.view(np.uint32), got[r:r + 1].view(np.uint32))
+
+
 @pytest.mark.parametrize("flags", [0, 2])
 def test_gemm_largest_k_smallest_n(lib, flags):
     """K = 8192 (64 chunks, eight scale groups) with N = 16 (a single tile per expert)."""

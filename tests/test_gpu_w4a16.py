@@ -50,12 +50,13 @@ def _oracle(a_bits, offsets, wn, wsc, N, K):
                                    lambda e: (wn[e * N:(e + 1) * N], wsc[e * N:(e + 1) * N]), N, K)
 
 
-@pytest.mark.parametrize("K", [2048, 4096])
-def test_w4a16_gemm_random_within_tolerance(lib, K):
+@pytest.mark.parametrize("K,N", [(2048, 512), (4096, 512), (640, 208), (1536, 208)])
+def test_w4a16_gemm_random_within_tolerance(lib, K, N):
+    """Random GEMMs within tolerance of the oracle; N = 208 leaves a partial item per
+    expert and K = 640 / 1536 gives scale groups of 1 / 4 chunks."""
     from nvfp4_block_scaled_gather_amd import binding as B
-    say("w4a16 gemm random K", K)
+    say("w4a16 gemm random K", K, "N", N)
     rng = np.random.default_rng(90 + K)
-    N = 512
     sizes = [1, 3, 0, 4, 5, 7, 16, 18, 40, 2]
     E = len(sizes)
     off = offsets_from_sizes(sizes)

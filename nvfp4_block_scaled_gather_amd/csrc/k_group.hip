@@ -299,11 +299,15 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
   }
   if (err) atomicOr(&s_err, err);
   __syncthreads();
-  // 2. bucket starts
-  block_exclusive_scan(cnt_e, E + 1, s_part);
-  block_exclusive_scan(cnt_t, T + 1, s_part);
+  // 2. bucket starts: one exclusive scan over both histograms (cnt_t follows cnt_e in LDS);
+  // the token part then starts at R (every assignment is counted once in cnt_e), taken off
+  block_exclusive_scan(cnt_e, (E + 1) + (T + 1), s_part);
   for (int k = tid; k < E + 1; k += kGroupThreads) expert_offsets[k] = cnt_e[k];
-  for (int k = tid; k < T + 1; k += kGroupThreads) tok_off[k] = cnt_t[k];
+  for (int k = tid; k < T + 1; k += kGroupThreads) {
+    const int v = cnt_t[k] - R;
+    cnt_t[k] = v;
+    tok_off[k] = v;
+  }
   if (tid == 0) *err_word = s_err;
   const int Rv = cnt_e[E];
   __syncthreads();

@@ -42,19 +42,16 @@ __device__ __forceinline__ uint32_t e4m3_encode_pos(float v) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// Nearest e2m1 code of a finite float, ties to even (code LSB 0), saturating at 6, sign
-// kept (grid {0, .5, 1, 1.5, 2, 3, 4, 6}).  Below 1 the grid is uniform with step 0.5, so
-// the code there is rint(2|q|) (exact doubling); from 1 on, the float32 significand is
-// rounded to one bit with round-half-even on the bit pattern (a carry moves into the
-// exponent), saturating at code 7.  The two regimes are combined without a select or a
-// branch: min(|q|, 1) feeds the first and max(|q|, 1) the second, and the two codes of 1
-// (2 each) overlap.
-__device__ __forceinline__ uint32_t e2m1_encode(float q) {
-  const float a = __builtin_fabsf(q);
-  const uint32_t sub = (uint32_t)__builtin_rintf(2.0f * __builtin_fminf(a, 1.0f));  // 0..2
-  const uint32_t b = __float_as_uint(__builtin_fmaxf(a, 1.0f));
-  const uint32_t nrm = min(((b + 0x1FFFFFu + ((b >> 22) & 1u)) >> 22) - 252u, 7u);  // 2..7
-  return (sub + nrm - 2u) | ((__float_as_uint(q) >> 28) & 8u);
+// Nearest e2m1 codes of eight finite floats, ties to even (code LSB 0), saturating at 6,
+// sign kept (-0 and negative values that round to 0 give code 8; grid {0, .5, 1, 1.5, 2,
+// 3, 4, 6}), packed as one word with element 2k in the low nibble of byte k.  This is the
+// hardware fp32 -> fp4 pack conversion at scale 1 (no scaling): compared on MI355X against
+// a software nearest-even encoder over every non-NaN fp32 bit pattern, with no difference.
+__device__ __forceinline__ uint32_t e2m1x8_encode(const float* q) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
 }
 
 // Eight e2m1 nibbles (one 32-bit word, element 2k in the low nibble of byte k) times a
@@ -246,15 +243,17 @@ __device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], in
         q = fmaf(fmaf(-d, q, x), y, q);
         return __builtin_copysignf(q, x);  // a zero quotient keeps x's sign, as x / d does
       };
+      float qv[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lo |= e2m1_encode(quot(v[k][e])) << (4 * e);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hi |= e2m1_encode(quot(v[k][8 + e])) << (4 * e);
+      for (int e = 0; e < 16; ++e) qv[e] = quot(v[k][e]);
+      lo = e2m1x8_encode(qv);
+      hi = e2m1x8_encode(qv + 8);
     } else if (d != 0.0f) {
+      float qv[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lo |= e2m1_encode(v[k][e] / d) << (4 * e);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) hi |= e2m1_encode(v[k][8 + e] / d) << (4 * e);
+      for (int e = 0; e < 16; ++e) qv[e] = v[k][e] / d;
+      lo = e2m1x8_encode(qv);
+      hi = e2m1x8_encode(qv + 8);
     }
     u32x2 pk = {lo, hi};
     *(u32x2*)(q + 8 * (size_t)b) = pk;

@@ -49,6 +49,7 @@
 #define MOE_W_CPOL 2  // cache policy of the weight-stream loads: non-temporal (read once)
 #endif
 
+
 namespace moe {
 
 constexpr int kGemmWaves = 4;
@@ -104,12 +105,12 @@ static size_t gemm_lds_bytes(int K, int rows, bool abf = false, int NS = 2,
 
 // The group of a workgroup's item.  Active groups are the experts whose group size is in
 // [gmin, gmax], in ascending expert id; item it of a launch belongs to active group
-// it / items_per_e.  When some group needs three or more passes over its weights (more than
-// 2 PR rows, a skewed batch), the groups of more than PR rows come first instead (each set
-// in ascending expert id), so that their long items start first rather than forming the
-// kernel's tail.  Wave 0 scans the offsets (512 experts per round, all loads of a round in
-// flight together) for group ai in plain order, counting the multi-pass groups and the
-// largest group on the way, and scans again only in the skewed case.  The lane that holds
+// it / items_per_e.  When some group needs two or more passes over its weights (more than
+// PR rows), the groups of more than PR rows come first instead (each set in ascending
+// expert id), so that their long items start first rather than forming the kernel's tail.
+// Wave 0 scans the offsets (512 experts per round, all loads of a round in flight
+// together) for group ai in plain order, counting the multi-pass groups on the way, and
+// scans again only when there are any.  The lane that holds
 // the group publishes (expert, first row, size) through LDS.  Returns false if there are at
 // most ai active groups (the workgroup has no item).  The order changes which workgroup
 // computes an output, never how.
@@ -124,10 +125,10 @@ __device__ __forceinline__ bool find_group(const GemmArgs& p, int ai, int* s_grp
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
     // Group number `target` among the active groups of the set `sel` (0: all; 1: more than
     // PR rows; 2: at most PR rows), in ascending expert id.  `count`: scan every expert and
-    // count the multi-pass groups and the largest group size.
-    int n_multi = 0, g_max = 0;
+    // count the multi-pass groups.
+    int n_multi = 0;
     auto scan = [&](int sel, int target, bool count) {
-      int n = 0, nm = 0, mx = 0;
+      int n = 0, nm = 0;
       bool found = false;
       for (int base = 0; base < p.E && (count || !found); base += 512) {  // uniform
         int lo[8], hi[8];
@@ -143,10 +144,7 @@ __device__ __forceinline__ bool find_group(const GemmArgs& p, int ai, int* s_grp
           const int sz = hi[u] - lo[u];
           const bool act = e < p.E && sz >= p.gmin && sz <= p.gmax;
           const bool mp = act && sz > PR;
-          if (count) {
-            nm += __popcll(__ballot(mp));
-            if (act) mx = max(mx, sz);
-          }
+          if (count) nm += __popcll(__ballot(mp));
           const bool a = act && (sel == 0 || mp == (sel == 1));
           const uint64_t m = __ballot(a);
           const int c = __popcll(m);
@@ -161,15 +159,11 @@ __device__ __forceinline__ bool find_group(const GemmArgs& p, int ai, int* s_grp
           n += c;
         }
       }
-      if (count) {
-        n_multi = nm;
-        for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
-        g_max = mx;
-      }
+      if (count) n_multi = nm;
       return found;
     };
     bool found = scan(0, ai, true);
-    if (n_multi > 0 && g_max > 2 * PR)  // skewed: the multi-pass groups first
+    if (n_multi > 0)  // the multi-pass groups first
       found = ai < n_multi ? scan(1, ai, false) : scan(2, ai - n_multi, false);
     if (lane == 0) s_grp[3] = found ? 1 : 0;
   }
@@ -490,9 +484,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
   const int tiles = SWI ? p.I / 16 : p.N / 16;
   const int per_item = SWI ? WAVES : WAVES * NS;
   const int items_per_e = (tiles + per_item - 1) / per_item;
+  const int item = blockIdx.x;
   ItemGroup g;
-  if (!find_group<PR>(p, blockIdx.x / items_per_e, s_grp, g)) return;  // uniform
-  const int t0 = (blockIdx.x % items_per_e) * per_item + wave * (SWI ? 1 : NS);
+  if (!find_group<PR>(p, item / items_per_e, s_grp, g)) return;  // uniform
+  const int t0 = (item % items_per_e) * per_item + wave * (SWI ? 1 : NS);
   const int nsv = SWI ? (t0 < tiles ? 2 : 0) : min(NS, tiles - t0);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;

@@ -217,7 +217,7 @@ __device__ __forceinline__ void stable_place(int n, int nkeys, int* bucket_start
 // LDS ints the grouping needs: the two histograms, plus the per-wave ones when parallel,
 // plus (cached) the R assignments, the grouped rows' output rows and the per-wave 64-bit
 // key masks of the ranking (two ints each, 8-byte aligned).
-constexpr int kCachedInts = 5;  // per assignment: key, src, dst, weight; grouped dst
+constexpr int kCachedInts = 7;  // per assignment: key, src, dst, weight; grouped dst, src, weight
 __host__ __device__ inline size_t group_lds_ints(int E, int T, bool parallel, int R, bool cached) {
   const size_t base = (size_t)(E + 1) + (size_t)(T + 1);
   const size_t keys = (size_t)((E > T ? E : T) + 1);
@@ -228,7 +228,10 @@ __host__ __device__ inline size_t group_lds_ints(int E, int T, bool parallel, in
 
 // The whole grouping, by one workgroup of kGroupThreads threads.  CACHED: the assignments
 // are read from global memory once, into LDS, and every later phase reads LDS (the phases
-// are otherwise a chain of dependent global round trips).
+// are otherwise a chain of dependent global round trips); the grouped rows and token lists
+// are placed in LDS too and written out in order, with coalesced stores (measured on
+// MI355X, scattered 4-byte stores of the placements from this one CU made the two placing
+// phases 2.5 us slower at 2303 assignments).
 template <bool CACHED>
 __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert, const int32_t* __restrict__ a_src,
                            const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R,
@@ -244,9 +247,12 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
   int* c_src = c_key + R;
   int* c_dst = c_src + R;
   float* c_w = (float*)(c_dst + R);
-  int* g_dst = c_dst + 2 * R;  // output row of grouped row i
+  int* g_dst = c_dst + 2 * R;  // output row of grouped row i (-1: dropped)
+  int* g_src = g_dst + R;      // its source row (-1: dropped)
+  float* g_w = (float*)(g_src + R);  // its router weight
+  int* t_rows = c_key;         // token lists, once the keys are no longer read
   // CACHED: the per-wave key masks of the ranking, after the cache (8-byte aligned)
-  const size_t mo = (size_t)(g_dst + R - lds);
+  const size_t mo = (size_t)(g_dst + 3 * R - lds);
   unsigned long long* masks =
       CACHED ? (unsigned long long*)(lds + ((mo + 1) & ~(size_t)1)) : nullptr;
   const int nkmax = (E > T ? E : T) + 1;
@@ -316,11 +322,15 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
     stable_place(R, E + 1, cnt_e, hist, nw, [&](int j) -> int { return c_key[j]; },
                  [&](int j, int pos) {
                    const bool ok = pos < Rv;
-                   row_src[pos] = ok ? c_src[j] : -1;
-                   row_dst[pos] = ok ? c_dst[j] : -1;
-                   row_w[pos] = ok ? c_w[j] : 0.f;
-                   if (ok) g_dst[pos] = c_dst[j];
+                   g_src[pos] = ok ? c_src[j] : -1;
+                   g_dst[pos] = ok ? c_dst[j] : -1;
+                   g_w[pos] = ok ? c_w[j] : 0.f;
                  }, masks);
+    for (int i = tid; i < R; i += kGroupThreads) {  // (after stable_place's barrier)
+      row_src[i] = g_src[i];
+      row_dst[i] = g_dst[i];
+      row_w[i] = g_w[i];
+    }
   } else {
     auto key_e = [&](int j) -> int {
       const int e = a_expert[j], sr = a_src[j], d = a_dst[j];
@@ -336,11 +346,14 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
   }
   // 4. token lists, ascending grouped row (the grouped rows' outputs are visible after
   // stable_place's barrier)
-  auto place_tok = [&](int i, int pos) { tok_rows[pos] = i; };
-  if constexpr (CACHED)
-    stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return g_dst[i]; }, place_tok, masks);
-  else
-    stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return row_dst[i]; }, place_tok);
+  if constexpr (CACHED) {
+    stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return g_dst[i]; },
+                 [&](int i, int pos) { t_rows[pos] = i; }, masks);
+    for (int i = tid; i < Rv; i += kGroupThreads) tok_rows[i] = t_rows[i];
+  } else {
+    stable_place(Rv, T, cnt_t, hist, nw, [&](int i) -> int { return row_dst[i]; },
+                 [&](int i, int pos) { tok_rows[pos] = i; });
+  }
 }
 
 __global__ __launch_bounds__(kGroupThreads) void k_group(

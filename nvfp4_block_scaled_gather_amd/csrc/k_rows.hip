@@ -9,25 +9,29 @@
 namespace moe {
 
 // ------------------------------------------------------------------------- quantize
-// One workgroup per output row i; its input is row row_map[i] (row_map == nullptr: row i;
-// a negative entry: an all-zero row); rows at or past *row_limit are all-zero rows.
-// Without a row map the row is loaded before the limit is known (it is in bounds either
-// way), so the two loads overlap.
+// nt threads per row (a multiple of 64), blockDim.x / nt rows per workgroup: output row i
+// (i < R) quantizes input row row_map[i] (row_map == nullptr: row i; a negative entry: an
+// all-zero row); rows at or past *row_limit are all-zero rows.  Without a row map the row
+// is loaded before the limit is known (it is in bounds either way), so the two loads
+// overlap.  Every thread joins the row-max barrier; only real rows store.
 template <int BPT>
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ in,
                                                   const int32_t* __restrict__ row_map,
-                                                  const int32_t* __restrict__ row_limit, int K,
-                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ sc,
+                                                  const int32_t* __restrict__ row_limit, int R,
+                                                  int K, int nt, uint8_t* __restrict__ q,
+                                                  uint8_t* __restrict__ sc,
                                                   float* __restrict__ row_gs) {
   __shared__ float s_red[4];
-  const int row = blockIdx.x;
-  const int src = row_map ? row_map[row] : row;
-  const bool live = !row_limit || row < *row_limit;
+  const int slot = threadIdx.x / nt, t = threadIdx.x - slot * nt;
+  const int row = blockIdx.x * (blockDim.x / nt) + slot;
+  const bool real = row < R;
+  const int src = !real ? -1 : row_map ? row_map[row] : row;
+  const bool live = real && (!row_limit || row < *row_limit);
   const int NB = K / 16;
   float v[BPT][16];
 #pragma unroll
   for (int k = 0; k < BPT; ++k) {
-    const int b = threadIdx.x + blockDim.x * k;
+    const int b = t + nt * k;
     u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
     if (b < NB && src >= 0) {
       const u32x4* p = (const u32x4*)(in + (size_t)src * K + 16 * b);
@@ -37,21 +41,23 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* __restrict__ i
     if (!live) w0 = w1 = u32x4{0u, 0u, 0u, 0u};
     bf16x16_to_f32(w0, w1, v[k]);
   }
-  const float amax = row_amax_threads<BPT>(v, threadIdx.x, blockDim.x, s_red);
-  quantize_row_store<BPT>(v, NB, threadIdx.x, blockDim.x, amax, q + (size_t)row * (K / 2),
-                          sc + (size_t)row * NB, row_gs + row);
+  const float amax = row_amax_threads<BPT>(v, t, nt, s_red + slot * (nt / 64));
+  if (real)
+    quantize_row_store<BPT>(v, NB, t, nt, amax, q + (size_t)row * (K / 2),
+                            sc + (size_t)row * NB, row_gs + row);
 }
 
 hipError_t launch_quantize(const uint16_t* in, const int32_t* row_map, const int32_t* row_limit,
                            int R, int K, uint8_t* q, uint8_t* sc, float* row_gs, hipStream_t s) {
   if (R == 0) return hipSuccess;
-  const int NB = K / 16, nt = row_threads(NB);
+  const int NB = K / 16;
+  const int nt = row_threads(NB);
   if (NB <= 256)
-    hipLaunchKernelGGL(k_quantize<1>, dim3(R), dim3(nt), 0, s, in, row_map, row_limit, K, q, sc,
-                       row_gs);
+    hipLaunchKernelGGL(k_quantize<1>, dim3(R), dim3(nt), 0, s, in, row_map, row_limit, R, K, nt, q,
+                       sc, row_gs);
   else
-    hipLaunchKernelGGL(k_quantize<2>, dim3(R), dim3(nt), 0, s, in, row_map, row_limit, K, q, sc,
-                       row_gs);
+    hipLaunchKernelGGL(k_quantize<2>, dim3(R), dim3(nt), 0, s, in, row_map, row_limit, R, K, nt, q,
+                       sc, row_gs);
   return hipGetLastError();
 }
 
@@ -162,6 +168,7 @@ hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* offset
 // on the other tokens of the batch.
 constexpr int kSumParts = 8;
 
+
 // Grid (T, ceil(H / 256)), 8 waves per workgroup (wave w = partial w), 4 columns per lane;
 // the coefficients of up to 64 rows are computed by the lanes in parallel.
 __global__ __launch_bounds__(64 * kSumParts) void k_scatter(
@@ -261,15 +268,22 @@ __global__ __launch_bounds__(256 * (WIDE ? 2 : 1)) void k_token_sum(
       const int p = base + kSumParts * lane;
       const int i = p < p1 ? tok_rows[p] : 0;
       const int n = min(64, (p1 - base + kSumParts - 1) / kSumParts);
-#pragma unroll 4
-      for (int k = 0; k < n; ++k) {
-        const int ik = __shfl(i, k, 64);
-        if (cv) {
-          const f32x4 v = *(const f32x4*)(yc + (size_t)ik * H + col);
-          acc[0] += v[0];
-          acc[1] += v[1];
-          acc[2] += v[2];
-          acc[3] += v[3];
+      // up to 16 rows' loads in flight before the first add (same order of the adds)
+      for (int k0 = 0; k0 < n; k0 += 16) {
+        f32x4 v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int ik = __builtin_amdgcn_readlane(i, (k0 + k) & 63);
+          if (k0 + k < n && cv) v[k] = *(const f32x4*)(yc + (size_t)ik * H + col);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (k0 + k < n && cv) {
+            acc[0] += v[k][0];
+            acc[1] += v[k][1];
+            acc[2] += v[k][2];
+            acc[3] += v[k][3];
+          }
         }
       }
     }

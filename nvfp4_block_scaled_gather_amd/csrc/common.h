@@ -262,6 +262,94 @@ __device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], in
   if (t == 0) *gs_out = gs;
 }
 
+// ------------------------------------------------------------------ one-wave grouping
+// The grouping of a small batch (at most 64 assignments) by one wave, shared by the
+// grouping launch and the decode-sized w13 GEMM, which groups in every workgroup.
+// Number of lanes p whose `sorted` value is below x, where `sorted` ascends with the lane
+// index (a binary search over the wave with shuffles; every lane of the wave must call it).
+__device__ __forceinline__ int wave_count_below(int sorted, int x) {
+  int i = 0;
+  for (int step = 32; step >= 1; step >>= 1)
+    if (__shfl(sorted, i + step - 1, 64) < x) i += step;
+  if (i == 63 && __shfl(sorted, 63, 64) < x) i = 64;
+  return i;
+}
+
+// The grouping of at most 64 assignments by wave 0 (lane j holds assignment j), with the
+// results of group_body: grouped position = the number of (key, index) pairs below the
+// lane's own (key = expert id, or E for a dropped assignment), by one comparison
+// per assignment; the token lists likewise by (output row, grouped position); the offsets
+// by binary searches of the sorted keys, which one ds_permute puts in lane order.
+__device__ __forceinline__ void group_small(const int32_t* __restrict__ a_expert,
+                                            const int32_t* __restrict__ a_src,
+                                            const int32_t* __restrict__ a_dst,
+                                            const float* __restrict__ a_w, int R, int E, int S,
+                                            int T, int32_t* __restrict__ expert_offsets,
+                                            int32_t* __restrict__ row_src,
+                                            int32_t* __restrict__ row_dst,
+                                            float* __restrict__ row_w,
+                                            int32_t* __restrict__ tok_off,
+                                            int32_t* __restrict__ tok_rows,
+                                            int32_t* __restrict__ err_word) {
+  if (threadIdx.x >= 64) return;  // wave 0 only (no barrier follows)
+  const int lane = threadIdx.x;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const bool act = lane < R;
+  int e = 0, sr = 0, d = 0;
+  float wv = 0.f;
+  if (act) {
+    e = a_expert[lane];
+    sr = a_src[lane];
+    d = a_dst[lane];
+    wv = a_w[lane];
+  }
+  int bad = 0;
+  if (act) {
+    if (e < 0 || e >= E) bad |= MOE_ERR_EXPERT;
+    if (sr < 0 || sr >= S) bad |= MOE_ERR_SRC;
+    if (d < 0 || d >= T) bad |= MOE_ERR_DST;
+  }
+  const bool valid = act && !bad;
+  const uint64_t vmask = __ballot(valid);
+  const int Rv = __popcll(vmask);
+  // 1. grouped position: stable order by (key, assignment index).  The counting loops run
+  // with every lane active: a lane read by readlane must hold the value computed for it,
+  // which the compiler only guarantees outside the branches that exclude that lane.
+  const int key = act ? (valid ? e : E) : 0x7FFFFFFF;
+  int rank = 0;
+  for (int k = 0; k < R; ++k) {
+    const int kk = __builtin_amdgcn_readlane(key, k);
+    rank += (kk < key || (kk == key && k < lane)) ? 1 : 0;
+  }
+  const int pos = act ? rank : lane;  // lanes past R keep their own slot: still a permutation
+  if (act) {
+    row_src[pos] = valid ? sr : -1;
+    row_dst[pos] = valid ? d : -1;
+    row_w[pos] = valid ? wv : 0.f;
+  }
+  // 2. expert offsets: grouped rows with a key below e (dropped ones carry key E)
+  const int skey = __builtin_amdgcn_ds_permute(4 * pos, key);  // lane p: the key at position p
+  for (int base = 0; base <= E; base += 64) {  // uniform: every lane joins the shuffles
+    const int c = wave_count_below(skey, base + lane);
+    if (base + lane <= E) expert_offsets[base + lane] = c;
+  }
+  // 3. token lists: valid rows in (output row, grouped position) order
+  const int tkey = valid ? d * 64 + pos : 0x7FFFFFFF;
+  int trank = 0;
+  for (int k = 0; k < R; ++k) trank += __builtin_amdgcn_readlane(tkey, k) < tkey ? 1 : 0;
+  // the other lanes keep distinct slots past Rv
+  const int tpos = valid ? trank : Rv + __popcll(~vmask & below);
+  if (valid) tok_rows[tpos] = pos;
+  const int sdst = __builtin_amdgcn_ds_permute(4 * tpos, valid ? d : 0x7FFFFFFF);
+  for (int base = 0; base <= T; base += 64) {
+    const int c = wave_count_below(sdst, base + lane);
+    if (base + lane <= T) tok_off[base + lane] = c;
+  }
+  int err = bad;
+  for (int m = 32; m >= 1; m >>= 1) err |= __shfl_xor(err, m, 64);
+  if (lane == 0) *err_word = err;
+}
+
 // Threads per row for NB scale blocks: a multiple of 64, at most 256.
 static inline int row_threads(int NB) {
   const int t = ((NB + 63) / 64) * 64;
@@ -308,6 +396,18 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, cons
                                       const uint8_t* w13, int I, int K, const float* g_gate,
                                       const float* g_up, const float* row_gs,
                                       const int32_t* gs_map, uint16_t* h, hipStream_t s);
+// The same for a batch of 1..32 assignments, with the grouping of launch_group and the
+// quantization of the source rows x [S, K] done inside the launch (the grouping outputs are
+// written as launch_group writes them; the quantized rows stay in LDS).
+hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const int32_t* a_src,
+                                               const int32_t* a_dst, const float* a_w, int R,
+                                               int E, int S, int T, const uint16_t* x,
+                                               int32_t* expert_offsets, int32_t* row_src,
+                                               int32_t* row_dst, float* row_w, int32_t* tok_off,
+                                               int32_t* tok_rows, int32_t* err_word,
+                                               const uint8_t* w13, int I, int K,
+                                               const float* g_gate, const float* g_up,
+                                               uint16_t* h, hipStream_t s);
 // W4A16 (bf16 activation rows ab [a_rows, K], through amap): the grouped GEMM (with c_w,
 // rows multiplied by c_w[i] * c_g[e]) and the w13 GEMM with the SwiGLU epilogue (gate / up
 // globals alone).

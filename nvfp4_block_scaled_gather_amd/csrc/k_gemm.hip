@@ -330,10 +330,14 @@ __device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC
 // the epilogue writes h = SwiGLU(gate, up) as bf16 (ggate, gup: the expert's gate / up
 // weight globals) instead of the fp32 products.  Otherwise, with p.c_w, ggate is the
 // expert's down global of the scatter-ready epilogue.
-template <int NS, int D, int S, bool SWI, bool ABF, int WAVES>
+//
+// FQ: the pass's rows are already quantized into the staging area and their row globals
+// are in s_rgs (the decode-sized w13 GEMM below); nothing is staged from global memory.
+template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, bool FQ = false>
 __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0,
-                                          uint8_t* s_q, uint8_t* s_s, float ggate, float gup) {
+                                          uint8_t* s_q, uint8_t* s_s, float ggate, float gup,
+                                          const float* s_rgs = nullptr) {
   static_assert(!SWI || NS == 2, "the SwiGLU epilogue pairs one gate and one up tile");
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, r = lane & 15;
@@ -355,7 +359,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     if (p.c_gs) ogs = p.c_gs[arow0 + r];
   }
 
-  stage_rows<ABF, WAVES>(p, arow0, nrows, s_q, s_s);
+  if (!FQ) stage_rows<ABF, WAVES>(p, arow0, nrows, s_q, s_s);
   __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
   __syncthreads();
 
@@ -436,7 +440,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     uint16_t* so = (uint16_t*)s_q;             // [16][WCH + 8] bf16 (within the output block)
     if (r < nrows && nsv > 0) {
       const int i = arow0 + r;
-      const float gs = p.row_gs ? p.row_gs[p.gs_map ? p.gs_map[i] : i] : 1.0f;
+      const float gs = FQ ? s_rgs[r] : p.row_gs ? p.row_gs[p.gs_map ? p.gs_map[i] : i] : 1.0f;
       const float cg = gs * ggate, cu = gs * gup;
       uint32_t hb[4];
 #pragma unroll
@@ -514,6 +518,138 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
     if (b) __syncthreads();  // the previous pass is done with the staged rows
     mfma_pass<NS, D, S, SWI, ABF, WAVES>(p, wt, nsv, g.r0 + b, min(PR, g.G - b), 16 * t0,
                                          s_q, s_s, ggate, gup);
+  }
+}
+
+// ------------------------------------------------------------------------- decode w13
+// A batch of at most kSmallGroupRows expert-rows (decode): the w13 GEMM with the SwiGLU
+// epilogue, every workgroup grouping the assignments itself with one wave (the one-wave
+// grouping's order) and quantizing its group's source rows straight into its staging area
+// with the grouping launch's quantizer, so the layer needs no grouping launch before this
+// one.  Workgroup 0 also writes the grouping's outputs for the later kernels.  The items,
+// passes and arithmetic are those of k_gemm_mfma's small-batch SwiGLU instance, so the
+// results are the same bits.  Workgroup ai / items_per_e takes the ai-th expert with rows
+// in ascending id (no multi-pass-first order: that only changes which workgroup computes
+// what).
+constexpr int kSmallGroupRows = 32;
+
+struct GroupArgs {
+  const int32_t* a_expert;
+  const int32_t* a_src;
+  const int32_t* a_dst;
+  const float* a_w;
+  int R, S, T;
+  const uint16_t* x;  // source rows [S, K] bf16
+  int32_t* offsets;
+  int32_t* row_src;
+  int32_t* row_dst;
+  float* row_w;
+  int32_t* tok_off;
+  int32_t* tok_rows;
+  int32_t* err;
+};
+
+template <int D, int S>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmArgs p, GroupArgs q) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_grp[4];
+  __shared__ int s_src[kSmallGroupRows];    // source rows of the group's grouped rows
+  __shared__ float s_rgs[kPassRows];        // row globals of the pass's rows
+  __shared__ float s_red[2 * kGemmWaves];   // row-max partials of two rows
+  uint8_t* s_q = smem;
+  uint8_t* s_s = s_q + kPassRows * q_stride(p.K);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles = p.I / 16, per_item = kGemmWaves;
+  const int items_per_e = (tiles + per_item - 1) / per_item;
+  const int ai = blockIdx.x / items_per_e;
+  if (wave == 0) {
+    if (blockIdx.x == 0)
+      group_small(q.a_expert, q.a_src, q.a_dst, q.a_w, q.R, p.E, q.S, q.T, q.offsets, q.row_src,
+                  q.row_dst, q.row_w, q.tok_off, q.tok_rows, q.err);
+    // grouped position of lane j's assignment: the number of (key, index) pairs below its
+    // own (the counting loop with every lane active, as in group_small)
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const bool act = lane < q.R;
+    int e = 0, sr = 0, d = 0;
+    if (act) {
+      e = q.a_expert[lane];
+      sr = q.a_src[lane];
+      d = q.a_dst[lane];
+    }
+    const bool valid = act && e >= 0 && e < p.E && sr >= 0 && sr < q.S && d >= 0 && d < q.T;
+    const int key = act ? (valid ? e : p.E) : 0x7FFFFFFF;
+    int rank = 0;
+    for (int k = 0; k < q.R; ++k) {
+      const int kk = __builtin_amdgcn_readlane(key, k);
+      rank += (kk < key || (kk == key && k < lane)) ? 1 : 0;
+    }
+    const int pos = act ? rank : lane;
+    const int skey = __builtin_amdgcn_ds_permute(4 * pos, key);  // lane p: key at position p
+    const int ssrc = __builtin_amdgcn_ds_permute(4 * pos, sr);
+    const int prev = __shfl_up(skey, 1, 64);
+    const bool first = skey < p.E && (lane == 0 || prev != skey);  // a group starts at lane
+    const uint64_t m = __ballot(first);
+    const uint64_t sel = __ballot(first && __popcll(m & below) == ai);
+    const bool found = sel != 0ull;  // uniform
+    if (found) {
+      const int r0 = __builtin_ctzll(sel);
+      const int eg = __builtin_amdgcn_readlane(skey, r0);
+      const int G = __popcll(__ballot(skey == eg));
+      if (lane >= r0 && lane < r0 + G) s_src[lane - r0] = ssrc;
+      if (lane == 0) {
+        s_grp[0] = eg;
+        s_grp[1] = r0;
+        s_grp[2] = G;
+      }
+    }
+    if (lane == 0) s_grp[3] = found ? 1 : 0;
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(s_grp[3]) == 0) return;  // uniform
+  const int eg = __builtin_amdgcn_readfirstlane(s_grp[0]);
+  const int r0 = __builtin_amdgcn_readfirstlane(s_grp[1]);
+  const int G = __builtin_amdgcn_readfirstlane(s_grp[2]);
+  const int t0 = (blockIdx.x % items_per_e) * per_item + wave;
+  const int nsv = t0 < tiles ? 2 : 0;
+  const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
+  const size_t tile_bytes = (size_t)9 * p.K;
+  const uint8_t* wt = p.w + (size_t)eg * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+  const float ggate = p.g_gate[eg], gup = p.g_up[eg];
+  const int NB = p.K / 16, t = threadIdx.x;
+  constexpr int NT = 64 * kGemmWaves;  // threads per row: block b = t + NT k of each row
+  for (int b = 0; b < G; b += kPassRows) {
+    if (b) __syncthreads();  // the previous pass is done with the staged rows
+    const int nrows = min(kPassRows, G - b);
+    // quantize the pass's rows into the staging area, two rows' loads in flight at a time
+    for (int r = 0; r < nrows; r += 2) {
+      float v[2][2][16];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int src = r + rr < nrows ? s_src[b + r + rr] : -1;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int blk = t + NT * k;
+          u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+          if (src >= 0 && blk < NB) {
+            const u32x4* px = (const u32x4*)(q.x + (size_t)src * p.K + 16 * blk);
+            w0 = px[0];
+            w1 = px[1];
+          }
+          bf16x16_to_f32(w0, w1, v[rr][k]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        // every thread joins the row-max barrier; only real rows store
+        const float amax = row_amax_threads<2>(v[rr], t, NT, s_red + rr * kGemmWaves);
+        if (r + rr < nrows)
+          quantize_row_store<2>(v[rr], NB, t, NT, amax, s_q + (r + rr) * q_stride(p.K),
+                                s_s + (r + rr) * s_stride(p.K), s_rgs + r + rr);
+      }
+    }
+    mfma_pass<2, D, S, true, false, kGemmWaves, true>(p, wt, nsv, r0 + b, nrows, 16 * t0, s_q,
+                                                      s_s, ggate, gup, s_rgs);
   }
 }
 
@@ -780,6 +916,39 @@ hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* a
   if (R <= 4 * E)
     return launch_mfma_t<2, MOE_GEMM_D, true, true, 8, kW4A16PassRows8>(a, 2 * 8, R, s);
   return launch_mfma_t<2, MOE_GEMM_D, true, true, kW4A16Waves>(a, 2 * kW4A16Waves, R, s);
+}
+
+hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const int32_t* a_src,
+                                               const int32_t* a_dst, const float* a_w, int R,
+                                               int E, int S, int T, const uint16_t* x,
+                                               int32_t* expert_offsets, int32_t* row_src,
+                                               int32_t* row_dst, float* row_w, int32_t* tok_off,
+                                               int32_t* tok_rows, int32_t* err_word,
+                                               const uint8_t* w13, int I, int K,
+                                               const float* g_gate, const float* g_up,
+                                               uint16_t* h, hipStream_t s) {
+  if (R < 1 || R > kSmallGroupRows) return hipErrorInvalidValue;
+  GemmArgs a{nullptr, nullptr, nullptr, S, expert_offsets, E, w13, 2 * I, K, nullptr, 1,
+             0x7FFFFFFF, g_gate, g_up, nullptr, nullptr, h, I};
+  const GroupArgs g{a_expert, a_src, a_dst, a_w, R, S, T, x, expert_offsets, row_src,
+                    row_dst, row_w, tok_off, tok_rows, err_word};
+  const size_t lds = gemm_lds_bytes(K, kPassRows);
+  const dim3 grid(gemm_grid(2 * kGemmWaves, a, R)), block(64 * kGemmWaves);
+  auto go = [&](auto kern) {
+    if (lds > 65536) {
+      const hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(kern, grid, block, lds, s, a, g);
+    return hipGetLastError();
+  };
+  switch (scale_group(K / 128)) {
+    case 8: return go(k_gemm_swiglu_grouping<8, 8>);
+    case 4: return go(k_gemm_swiglu_grouping<4, 4>);
+    case 2: return go(k_gemm_swiglu_grouping<2, 2>);
+    default: return go(k_gemm_swiglu_grouping<1, 1>);
+  }
 }
 
 }  // namespace moe

@@ -21,91 +21,6 @@ constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kSmallGroupRows = 32;  // group_small: at most one assignment per lane
 
-// Number of lanes p whose `sorted` value is below x, where `sorted` ascends with the lane
-// index (a binary search over the wave with shuffles; every lane of the wave must call it).
-__device__ __forceinline__ int wave_count_below(int sorted, int x) {
-  int i = 0;
-  for (int step = 32; step >= 1; step >>= 1)
-    if (__shfl(sorted, i + step - 1, 64) < x) i += step;
-  if (i == 63 && __shfl(sorted, 63, 64) < x) i = 64;
-  return i;
-}
-
-// The grouping of at most 64 assignments by wave 0 (lane j holds assignment j), with the
-// results of group_body: grouped position = the number of (key, index) pairs below the
-// lane's own (key = expert id, or E for a dropped assignment), by one comparison
-// per assignment; the token lists likewise by (output row, grouped position); the offsets
-// by binary searches of the sorted keys, which one ds_permute puts in lane order.
-__device__ __forceinline__ void group_small(const int32_t* __restrict__ a_expert,
-                                            const int32_t* __restrict__ a_src,
-                                            const int32_t* __restrict__ a_dst,
-                                            const float* __restrict__ a_w, int R, int E, int S,
-                                            int T, int32_t* __restrict__ expert_offsets,
-                                            int32_t* __restrict__ row_src,
-                                            int32_t* __restrict__ row_dst,
-                                            float* __restrict__ row_w,
-                                            int32_t* __restrict__ tok_off,
-                                            int32_t* __restrict__ tok_rows,
-                                            int32_t* __restrict__ err_word) {
-  if (threadIdx.x >= 64) return;  // wave 0 only (no barrier follows)
-  const int lane = threadIdx.x;
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  const bool act = lane < R;
-  int e = 0, sr = 0, d = 0;
-  float wv = 0.f;
-  if (act) {
-    e = a_expert[lane];
-    sr = a_src[lane];
-    d = a_dst[lane];
-    wv = a_w[lane];
-  }
-  int bad = 0;
-  if (act) {
-    if (e < 0 || e >= E) bad |= MOE_ERR_EXPERT;
-    if (sr < 0 || sr >= S) bad |= MOE_ERR_SRC;
-    if (d < 0 || d >= T) bad |= MOE_ERR_DST;
-  }
-  const bool valid = act && !bad;
-  const uint64_t vmask = __ballot(valid);
-  const int Rv = __popcll(vmask);
-  // 1. grouped position: stable order by (key, assignment index).  The counting loops run
-  // with every lane active: a lane read by readlane must hold the value computed for it,
-  // which the compiler only guarantees outside the branches that exclude that lane.
-  const int key = act ? (valid ? e : E) : 0x7FFFFFFF;
-  int rank = 0;
-  for (int k = 0; k < R; ++k) {
-    const int kk = __builtin_amdgcn_readlane(key, k);
-    rank += (kk < key || (kk == key && k < lane)) ? 1 : 0;
-  }
-  const int pos = act ? rank : lane;  // lanes past R keep their own slot: still a permutation
-  if (act) {
-    row_src[pos] = valid ? sr : -1;
-    row_dst[pos] = valid ? d : -1;
-    row_w[pos] = valid ? wv : 0.f;
-  }
-  // 2. expert offsets: grouped rows with a key below e (dropped ones carry key E)
-  const int skey = __builtin_amdgcn_ds_permute(4 * pos, key);  // lane p: the key at position p
-  for (int base = 0; base <= E; base += 64) {  // uniform: every lane joins the shuffles
-    const int c = wave_count_below(skey, base + lane);
-    if (base + lane <= E) expert_offsets[base + lane] = c;
-  }
-  // 3. token lists: valid rows in (output row, grouped position) order
-  const int tkey = valid ? d * 64 + pos : 0x7FFFFFFF;
-  int trank = 0;
-  for (int k = 0; k < R; ++k) trank += __builtin_amdgcn_readlane(tkey, k) < tkey ? 1 : 0;
-  // the other lanes keep distinct slots past Rv
-  const int tpos = valid ? trank : Rv + __popcll(~vmask & below);
-  if (valid) tok_rows[tpos] = pos;
-  const int sdst = __builtin_amdgcn_ds_permute(4 * tpos, valid ? d : 0x7FFFFFFF);
-  for (int base = 0; base <= T; base += 64) {
-    const int c = wave_count_below(sdst, base + lane);
-    if (base + lane <= T) tok_off[base + lane] = c;
-  }
-  int err = bad;
-  for (int m = 32; m >= 1; m >>= 1) err |= __shfl_xor(err, m, 64);
-  if (lane == 0) *err_word = err;
-}
-
 // Lanes of the wave whose `key` equals this lane's key (keys < 2^bits).
 __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits, bool active) {
   uint64_t m = __ballot(active);

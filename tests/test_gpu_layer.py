@@ -107,6 +107,34 @@ def test_layer_equals_separate_calls(lib, flags, gemv_max):
     assert np.array_equal(got, _composed(B, dl, flags, gemv_max))
 
 
+@pytest.mark.parametrize("R,hot", [(1, 0), (17, 17), (32, 20), (33, 20)])
+def test_decode_sized_layer_equals_separate_calls(lib, R, hot):
+    """Batches of at most 32 assignments take the w13 launch that groups and quantizes by
+    itself (no grouping launch): bit-identical to the separate entry points, with a group
+    of more than 16 rows (two passes), two invalid assignments (dropped, error bits set) and
+    33 assignments (the other path) as edge cases."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("decode-sized layer vs separate calls", R, hot)
+    base = W.make_workload("ragged2303", E=24, H=512, I=256)
+    sel = np.arange(R)
+    a_expert = base.a_expert[sel].copy()
+    a_expert[:hot] = 3  # one group of `hot` rows
+    a_dst = base.a_dst[sel].copy()
+    if R >= 17:
+        a_expert[5] = base.E      # expert id out of range
+        a_dst[6] = base.T         # output row out of range
+    wl = W.Workload(**{**base.__dict__, "a_expert": a_expert, "a_src": base.a_src[sel],
+                       "a_dst": a_dst, "a_w": base.a_w[sel]})
+    dl = L.DeviceLayer(wl, flags=0, gemv_max_rows=0)
+    got = host(dl.forward())
+    sync()
+    err = dl.device_error()
+    assert err == (0 if R < 17 else B.MOE_ERR_EXPERT | B.MOE_ERR_DST), err
+    assert np.array_equal(got, _composed(B, dl, 0, 0))
+
+
 @pytest.mark.parametrize("flags", [1, 2])
 def test_layer_batch_parity_and_determinism(lib, flags):
     """[GG] "Proof" / batch parity: a token's output is the same

@@ -408,6 +408,13 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
                                                const uint8_t* w13, int I, int K,
                                                const float* g_gate, const float* g_up,
                                                uint16_t* h, hipStream_t s);
+// The w2 GEMM with the scatter-ready epilogue for a batch of 1..32 grouped rows, quantizing
+// its rows of h [R, K] (bf16, grouped order) itself: the bits of launch_quantize on h
+// followed by launch_grouped_gemm with c_gs = the quantized rows' globals.
+hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expert_offsets,
+                                          int E, int R, const uint8_t* w2, int N, int K,
+                                          float* out, const float* row_w, const float* g_down,
+                                          hipStream_t s);
 // W4A16 (bf16 activation rows ab [a_rows, K], through amap): the grouped GEMM (with c_w,
 // rows multiplied by c_w[i] * c_g[e]) and the w13 GEMM with the SwiGLU epilogue (gate / up
 // globals alone).

@@ -356,7 +356,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   float ow = 0.f, ogs = 1.f;
   if (!SWI && p.c_w && r < nrows) {
     ow = p.c_w[arow0 + r];
-    if (p.c_gs) ogs = p.c_gs[arow0 + r];
+    if (!FQ && p.c_gs) ogs = p.c_gs[arow0 + r];
   }
 
   if (!FQ) stage_rows<ABF, WAVES>(p, arow0, nrows, s_q, s_s);
@@ -463,7 +463,8 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     constexpr int LPR = WC / 4;                // 16-byte pieces per row
     float* so = (float*)s_q;                   // [16][WC + 4] floats (the output block)
     if (r < nrows) {
-      const float cf = ow * ggate * ogs;  // ggate: the expert's down global here
+      // ggate: the expert's down global here; FQ: the row global just computed
+      const float cf = ow * ggate * (FQ ? s_rgs[r] : ogs);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         f32x4 v = acc[s];
@@ -532,6 +533,45 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
 // in ascending id (no multi-pass-first order: that only changes which workgroup computes
 // what).
 constexpr int kSmallGroupRows = 32;
+
+// Quantize nrows bf16 rows of K columns (row_ptr(r): row r's first element, nullptr: an
+// all-zero row) into the staging area, row r at s_q + r q_stride(K) / s_s + r s_stride(K)
+// and its row global at s_rgs[r], with the quantizer of the row kernels (every thread of
+// the workgroup takes part; two rows' loads in flight at a time).  The caller synchronizes
+// before the staged rows are read.
+template <class RowPtr>
+__device__ __forceinline__ void quantize_rows_to_lds(RowPtr row_ptr, int nrows, int K,
+                                                     uint8_t* s_q, uint8_t* s_s, float* s_rgs,
+                                                     float* s_red) {
+  constexpr int NT = 64 * kGemmWaves;  // threads per row: block b = t + NT k of each row
+  const int NB = K / 16, t = threadIdx.x;
+  for (int r = 0; r < nrows; r += 2) {
+    float v[2][2][16];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const uint16_t* src = r + rr < nrows ? row_ptr(r + rr) : nullptr;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int blk = t + NT * k;
+        u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+        if (src && blk < NB) {
+          const u32x4* px = (const u32x4*)(src + 16 * blk);
+          w0 = px[0];
+          w1 = px[1];
+        }
+        bf16x16_to_f32(w0, w1, v[rr][k]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      // every thread joins the row-max barrier; only real rows store
+      const float amax = row_amax_threads<2>(v[rr], t, NT, s_red + rr * kGemmWaves);
+      if (r + rr < nrows)
+        quantize_row_store<2>(v[rr], NB, t, NT, amax, s_q + (r + rr) * q_stride(K),
+                              s_s + (r + rr) * s_stride(K), s_rgs + r + rr);
+    }
+  }
+}
 
 struct GroupArgs {
   const int32_t* a_expert;
@@ -616,40 +656,50 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
   const size_t tile_bytes = (size_t)9 * p.K;
   const uint8_t* wt = p.w + (size_t)eg * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
   const float ggate = p.g_gate[eg], gup = p.g_up[eg];
-  const int NB = p.K / 16, t = threadIdx.x;
-  constexpr int NT = 64 * kGemmWaves;  // threads per row: block b = t + NT k of each row
   for (int b = 0; b < G; b += kPassRows) {
     if (b) __syncthreads();  // the previous pass is done with the staged rows
     const int nrows = min(kPassRows, G - b);
-    // quantize the pass's rows into the staging area, two rows' loads in flight at a time
-    for (int r = 0; r < nrows; r += 2) {
-      float v[2][2][16];
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int src = r + rr < nrows ? s_src[b + r + rr] : -1;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int blk = t + NT * k;
-          u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-          if (src >= 0 && blk < NB) {
-            const u32x4* px = (const u32x4*)(q.x + (size_t)src * p.K + 16 * blk);
-            w0 = px[0];
-            w1 = px[1];
-          }
-          bf16x16_to_f32(w0, w1, v[rr][k]);
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        // every thread joins the row-max barrier; only real rows store
-        const float amax = row_amax_threads<2>(v[rr], t, NT, s_red + rr * kGemmWaves);
-        if (r + rr < nrows)
-          quantize_row_store<2>(v[rr], NB, t, NT, amax, s_q + (r + rr) * q_stride(p.K),
-                                s_s + (r + rr) * s_stride(p.K), s_rgs + r + rr);
-      }
-    }
+    quantize_rows_to_lds([&](int r) { return q.x + (size_t)s_src[b + r] * p.K; }, nrows, p.K, s_q,
+                         s_s, s_rgs, s_red);
     mfma_pass<2, D, S, true, false, kGemmWaves, true>(p, wt, nsv, r0 + b, nrows, 16 * t0, s_q,
                                                       s_s, ggate, gup, s_rgs);
+  }
+}
+
+// A batch of at most kSmallGroupRows expert-rows: the w2 GEMM with the scatter-ready
+// epilogue, each workgroup quantizing its group's rows of h (bf16, grouped order) straight
+// into its staging area with the quantizer of the row kernels, so the layer needs no
+// quantization launch between the two GEMMs; the scatter coefficient takes the row global
+// it has just computed.  Items, passes and arithmetic are those of k_gemm_mfma's
+// small-batch instance: the same bits.
+template <int D, int S>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_quantizing(GemmArgs p,
+                                                                     const uint16_t* __restrict__ h) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_grp[4];
+  __shared__ float s_rgs[kPassRows];
+  __shared__ float s_red[2 * kGemmWaves];
+  uint8_t* s_q = smem;
+  uint8_t* s_s = s_q + kPassRows * q_stride(p.K);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles = p.N / 16, per_item = kGemmWaves;  // one tile per wave
+  const int items_per_e = (tiles + per_item - 1) / per_item;
+  ItemGroup g;
+  if (!find_group<kPassRows>(p, blockIdx.x / items_per_e, s_grp, g)) return;  // uniform
+  const int t0 = (blockIdx.x % items_per_e) * per_item + wave;
+  const int nsv = min(1, tiles - t0);
+  const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
+  const size_t tile_bytes = (size_t)9 * p.K;
+  const uint8_t* wt = p.w + (size_t)g.e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
+  const float gdown = p.c_g[g.e];
+  for (int b = 0; b < g.G; b += kPassRows) {
+    if (b) __syncthreads();  // the previous pass is done with the staged rows
+    const int nrows = min(kPassRows, g.G - b);
+    const int row0 = g.r0 + b;
+    quantize_rows_to_lds([&](int r) { return h + (size_t)(row0 + r) * p.K; }, nrows, p.K, s_q,
+                         s_s, s_rgs, s_red);
+    mfma_pass<1, D, S, false, false, kGemmWaves, true>(p, wt, nsv, row0, nrows, 16 * t0, s_q,
+                                                       s_s, gdown, 0.f, s_rgs);
   }
 }
 
@@ -948,6 +998,33 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
     case 4: return go(k_gemm_swiglu_grouping<4, 4>);
     case 2: return go(k_gemm_swiglu_grouping<2, 2>);
     default: return go(k_gemm_swiglu_grouping<1, 1>);
+  }
+}
+
+hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expert_offsets,
+                                          int E, int R, const uint8_t* w2, int N, int K,
+                                          float* out, const float* row_w, const float* g_down,
+                                          hipStream_t s) {
+  if (R < 1 || R > kSmallGroupRows) return hipErrorInvalidValue;
+  GemmArgs a{nullptr, nullptr, nullptr, R, expert_offsets, E, w2, N, K, out, 1, 0x7FFFFFFF};
+  a.c_w = row_w;
+  a.c_g = g_down;
+  const size_t lds = gemm_lds_bytes(K, kPassRows, false, 1);
+  const dim3 grid(gemm_grid(kGemmWaves, a, R)), block(64 * kGemmWaves);
+  auto go = [&](auto kern) {
+    if (lds > 65536) {
+      const hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(kern, grid, block, lds, s, a, h);
+    return hipGetLastError();
+  };
+  switch (scale_group(K / 128)) {
+    case 8: return go(k_gemm_quantizing<8, 8>);
+    case 4: return go(k_gemm_quantizing<4, 4>);
+    case 2: return go(k_gemm_quantizing<2, 2>);
+    default: return go(k_gemm_quantizing<1, 1>);
   }
 }
 

@@ -221,9 +221,10 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
  * the row, so this equals gather-then-quantize).  When every group runs on the MFMA path
  * (the default), SwiGLU runs in the w13 GEMM's epilogue and h is quantized by one small
  * launch; with GEMV groups, SwiGLU and the second quantization are one kernel.  A batch
- * of 1 to 32 assignments on the MFMA path has no grouping launch: each workgroup of the w13
- * GEMM groups the assignments and quantizes its group's source rows itself, and one of
- * them writes the grouping's outputs (workspace) for the later launches.  The w2 GEMM
+ * of 1 to 32 assignments on the MFMA path has no grouping and no quantization launch: each
+ * workgroup of the w13 GEMM groups the assignments and quantizes its group's source rows
+ * itself (one of them writes the grouping's outputs to the workspace for the later
+ * launches), and each workgroup of the w2 GEMM quantizes its group's rows of h itself.  The w2 GEMM
  * writes each row's weighted scatter term, summed per token by the last launch.  The
  * results are bit-identical to calling the separate entry points in sequence.
  *

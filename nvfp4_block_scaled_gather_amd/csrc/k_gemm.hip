@@ -26,6 +26,10 @@
 //    k-quarters are summed across lanes at the end in a fixed tree.
 // Both dequantize exactly (dequant8 in common.h) and accumulate in fp32 in an order that
 // depends only on (N, K) and the path, never on the other rows of the group.
+// Two more kernels serve the layer's decode-sized batches (at most 32 assignments) on the
+// MFMA path with k_gemm_mfma's passes and arithmetic: k_gemm_swiglu_grouping (w13 with the
+// SwiGLU epilogue, each workgroup grouping the assignments and quantizing its group's
+// source rows itself) and k_gemm_quantizing (w2, each workgroup quantizing its rows of h).
 //
 // Outputs are written as whole rows of the workgroup's block (store_out): measured on
 // MI355X, write-back stores that are later evicted from L2 in the middle of the weight

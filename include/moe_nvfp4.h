@@ -260,7 +260,9 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S,
  * bf16 source rows (grouped row i reads source row row_src[i]) with SwiGLU in its
  * epilogue, h = bf16( silu(g_gate[e] * acc_gate) * g_up[e] * acc_up ) (bf16 activations
  * carry no row global); the w2 GEMM over bf16 h; the scatter-add weighted by
- * row_w[i] * g_down[e].
+ * row_w[i] * g_down[e].  A batch of 1 to 32 assignments has no grouping launch: each
+ * workgroup of the w13 GEMM groups the assignments itself (one of them writes the
+ * grouping's outputs to the workspace), with the same results.
  * Same descriptor (flags and gemv_max_rows are not used: every group runs on the bf16
  * matrix cores), arguments, workspace (moe_layer_workspace_bytes) and error word as
  * moe_layer_forward.  Limits: those of moe_layer_forward, plus H <= 4096 and I <= 4096.

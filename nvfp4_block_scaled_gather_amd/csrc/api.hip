@@ -305,7 +305,7 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
                                                  w.offsets, w.row_src, w.row_dst, w.row_w,
                                                  w.tok_off, w.tok_rows, w.err,
                                                  (const uint8_t*)L->w13_packed, I, H, L->g_gate,
-                                                 L->g_up, w.h16, stream);
+                                                 L->g_up, w.h16, stream, false);
     if (e != hipSuccess) return hip_status(e, "layer: grouping w13 GEMM + SwiGLU launch");
   } else {
     // grouping + NVFP4 quantization of the S source rows (one launch); the w13 GEMM reads
@@ -379,14 +379,28 @@ int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
   REQUIRE(aligned(x, 16) && aligned(out, 8) && aligned(L->w13_packed, 16) && aligned(L->w2_packed, 16),
           MOE_EINVAL, "layer: x / weights must be 16-byte, out 8-byte aligned");
   const int E = L->E, H = L->H, I = L->I;
-  hipError_t e = moe::launch_group(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
-                                   w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, stream);
-  if (e != hipSuccess) return hip_status(e, "layer: group launch");
+  hipError_t e;
+  if (R >= 1 && R <= 32) {
+    // a decode-sized batch: the w13 launch groups by itself (no grouping launch); the same
+    // bits as the sequence below
+    e = moe::launch_grouped_gemm_swiglu_grouping(a_expert, a_src, a_dst, a_w, R, E, S, T, x,
+                                                 w.offsets, w.row_src, w.row_dst, w.row_w,
+                                                 w.tok_off, w.tok_rows, w.err,
+                                                 (const uint8_t*)L->w13_packed, I, H, L->g_gate,
+                                                 L->g_up, w.h16, stream, true);
+    if (e != hipSuccess) return hip_status(e, "layer: W4A16 grouping w13 GEMM + SwiGLU launch");
+  } else {
+    e = moe::launch_group(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
+                          w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, stream);
+    if (e != hipSuccess) return hip_status(e, "layer: group launch");
+    if (R > 0) {
+      e = moe::launch_grouped_gemm_swiglu_w4a16(x, w.row_src, S, w.offsets, E, R,
+                                                (const uint8_t*)L->w13_packed, I, H, L->g_gate,
+                                                L->g_up, w.h16, stream);
+      if (e != hipSuccess) return hip_status(e, "layer: W4A16 w13 GEMM + SwiGLU launch");
+    }
+  }
   if (R > 0) {
-    e = moe::launch_grouped_gemm_swiglu_w4a16(x, w.row_src, S, w.offsets, E, R,
-                                              (const uint8_t*)L->w13_packed, I, H, L->g_gate,
-                                              L->g_up, w.h16, stream);
-    if (e != hipSuccess) return hip_status(e, "layer: W4A16 w13 GEMM + SwiGLU launch");
     e = moe::launch_grouped_gemm_w4a16(w.h16, nullptr, R, w.offsets, E, R,
                                        (const uint8_t*)L->w2_packed, H, I, w.acc, stream, w.row_w,
                                        L->g_down);

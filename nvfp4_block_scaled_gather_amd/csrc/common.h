@@ -398,7 +398,8 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, cons
                                       const int32_t* gs_map, uint16_t* h, hipStream_t s);
 // The same for a batch of 1..32 assignments, with the grouping of launch_group and the
 // quantization of the source rows x [S, K] done inside the launch (the grouping outputs are
-// written as launch_group writes them; the quantized rows stay in LDS).
+// written as launch_group writes them; the quantized rows stay in LDS).  bf16_acts: the
+// W4A16 arithmetic (launch_grouped_gemm_swiglu_w4a16), the rows used as bf16.
 hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const int32_t* a_src,
                                                const int32_t* a_dst, const float* a_w, int R,
                                                int E, int S, int T, const uint16_t* x,
@@ -407,7 +408,7 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
                                                int32_t* tok_rows, int32_t* err_word,
                                                const uint8_t* w13, int I, int K,
                                                const float* g_gate, const float* g_up,
-                                               uint16_t* h, hipStream_t s);
+                                               uint16_t* h, hipStream_t s, bool bf16_acts);
 // The w2 GEMM with the scatter-ready epilogue for a batch of 1..32 grouped rows, quantizing
 // its rows of h [R, K] (bf16, grouped order) itself: the bits of launch_quantize on h
 // followed by launch_grouped_gemm with c_gs = the quantized rows' globals.

@@ -613,15 +613,18 @@ struct GroupArgs {
   int32_t* err;
 };
 
-template <int D, int S>
+// ABF (W4A16): the source rows are bf16 activations used as they are (copied into the
+// staging area, row global 1), in passes of 4 rows like the small-batch W4A16 instance.
+template <int D, int S, bool ABF>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmArgs p, GroupArgs q) {
+  constexpr int PR = ABF ? 4 : kPassRows;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_grp[4];
   __shared__ int s_src[kSmallGroupRows];    // source rows of the group's grouped rows
   __shared__ float s_rgs[kPassRows];        // row globals of the pass's rows
   __shared__ float s_red[2 * kGemmWaves];   // row-max partials of two rows
   uint8_t* s_q = smem;
-  uint8_t* s_s = s_q + kPassRows * q_stride(p.K);
+  uint8_t* s_s = s_q + PR * q_stride(p.K);  // NVFP4 scales (unused with ABF)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tiles = p.I / 16, per_item = kGemmWaves;
@@ -680,13 +683,23 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
   const size_t tile_bytes = (size_t)9 * p.K;
   const uint8_t* wt = p.w + (size_t)eg * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
   const float ggate = p.g_gate[eg], gup = p.g_up[eg];
-  for (int b = 0; b < G; b += kPassRows) {
+  for (int b = 0; b < G; b += PR) {
     if (b) __syncthreads();  // the previous pass is done with the staged rows
-    const int nrows = min(kPassRows, G - b);
-    quantize_rows_to_lds([&](int r) { return q.x + (size_t)s_src[b + r] * p.K; }, nrows, p.K, s_q,
-                         s_s, s_rgs, s_red);
-    mfma_pass<2, D, S, true, false, kGemmWaves, true>(p, wt, nsv, r0 + b, nrows, 16 * t0, s_q,
-                                                      s_s, ggate, gup, s_rgs);
+    const int nrows = min(PR, G - b);
+    if constexpr (ABF) {
+      const int pieces = p.K / 8;  // 16-byte pieces of a bf16 row
+      for (int u = threadIdx.x; u < nrows * pieces; u += 64 * kGemmWaves) {
+        const int r = u / pieces, c = u - r * pieces;
+        const u32x4 v = *(const u32x4*)(q.x + (size_t)s_src[b + r] * p.K + 8 * c);
+        *(u32x4*)(s_q + r * b_stride(p.K) + 16 * c) = v;
+      }
+      if (threadIdx.x < nrows) s_rgs[threadIdx.x] = 1.0f;
+    } else {
+      quantize_rows_to_lds([&](int r) { return q.x + (size_t)s_src[b + r] * p.K; }, nrows, p.K,
+                           s_q, s_s, s_rgs, s_red);
+    }
+    mfma_pass<2, D, S, true, ABF, kGemmWaves, true>(p, wt, nsv, r0 + b, nrows, 16 * t0, s_q,
+                                                    s_s, ggate, gup, s_rgs);
   }
 }
 
@@ -992,21 +1005,21 @@ hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* a
   return launch_mfma_t<2, MOE_GEMM_D, true, true, kW4A16Waves>(a, 2 * kW4A16Waves, R, s);
 }
 
-hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const int32_t* a_src,
-                                               const int32_t* a_dst, const float* a_w, int R,
-                                               int E, int S, int T, const uint16_t* x,
-                                               int32_t* expert_offsets, int32_t* row_src,
-                                               int32_t* row_dst, float* row_w, int32_t* tok_off,
-                                               int32_t* tok_rows, int32_t* err_word,
-                                               const uint8_t* w13, int I, int K,
-                                               const float* g_gate, const float* g_up,
-                                               uint16_t* h, hipStream_t s) {
+template <bool ABF>
+static hipError_t launch_swiglu_grouping_t(const int32_t* a_expert, const int32_t* a_src,
+                                           const int32_t* a_dst, const float* a_w, int R, int E,
+                                           int S, int T, const uint16_t* x,
+                                           int32_t* expert_offsets, int32_t* row_src,
+                                           int32_t* row_dst, float* row_w, int32_t* tok_off,
+                                           int32_t* tok_rows, int32_t* err_word,
+                                           const uint8_t* w13, int I, int K, const float* g_gate,
+                                           const float* g_up, uint16_t* h, hipStream_t s) {
   if (R < 1 || R > kSmallGroupRows) return hipErrorInvalidValue;
   GemmArgs a{nullptr, nullptr, nullptr, S, expert_offsets, E, w13, 2 * I, K, nullptr, 1,
              0x7FFFFFFF, g_gate, g_up, nullptr, nullptr, h, I};
   const GroupArgs g{a_expert, a_src, a_dst, a_w, R, S, T, x, expert_offsets, row_src,
                     row_dst, row_w, tok_off, tok_rows, err_word};
-  const size_t lds = gemm_lds_bytes(K, kPassRows);
+  const size_t lds = gemm_lds_bytes(K, ABF ? 4 : kPassRows, ABF);
   const dim3 grid(gemm_grid(2 * kGemmWaves, a, R)), block(64 * kGemmWaves);
   auto go = [&](auto kern) {
     if (lds > 65536) {
@@ -1018,11 +1031,25 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
     return hipGetLastError();
   };
   switch (scale_group(K / 128)) {
-    case 8: return go(k_gemm_swiglu_grouping<8, 8>);
-    case 4: return go(k_gemm_swiglu_grouping<4, 4>);
-    case 2: return go(k_gemm_swiglu_grouping<2, 2>);
-    default: return go(k_gemm_swiglu_grouping<1, 1>);
+    case 8: return go(k_gemm_swiglu_grouping<8, 8, ABF>);
+    case 4: return go(k_gemm_swiglu_grouping<4, 4, ABF>);
+    case 2: return go(k_gemm_swiglu_grouping<2, 2, ABF>);
+    default: return go(k_gemm_swiglu_grouping<1, 1, ABF>);
   }
+}
+
+hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const int32_t* a_src,
+                                               const int32_t* a_dst, const float* a_w, int R,
+                                               int E, int S, int T, const uint16_t* x,
+                                               int32_t* expert_offsets, int32_t* row_src,
+                                               int32_t* row_dst, float* row_w, int32_t* tok_off,
+                                               int32_t* tok_rows, int32_t* err_word,
+                                               const uint8_t* w13, int I, int K,
+                                               const float* g_gate, const float* g_up,
+                                               uint16_t* h, hipStream_t s, bool bf16_acts) {
+  auto f = bf16_acts ? launch_swiglu_grouping_t<true> : launch_swiglu_grouping_t<false>;
+  return f(a_expert, a_src, a_dst, a_w, R, E, S, T, x, expert_offsets, row_src, row_dst, row_w,
+           tok_off, tok_rows, err_word, w13, I, K, g_gate, g_up, h, s);
 }
 
 hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expert_offsets,

@@ -294,30 +294,31 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
   hipError_t e;
   const bool all_mfma = L->flags == MOE_PATH_FORCE_MFMA ||
                         (L->flags == MOE_PATH_AUTO && L->gemv_max_rows == 0);
-  // A decode-sized batch (1..32 assignments) on the MFMA path: the w13 GEMM launch groups
-  // and quantizes by itself and the w2 GEMM launch quantizes h by itself (two launches
-  // fewer, measured on MI355X to save their time at one to four tokens); the same bits as
-  // the sequence below.
-  const bool fused_grouping = all_mfma && R >= 1 && R <= 32;
-  if (fused_grouping) {
-    // h goes to its own buffer: the w2 launch reads it while writing its terms into acc
+  if (all_mfma && R >= 1 && R <= 32) {
+    // A decode-sized batch on the MFMA path, three launches: the w13 GEMM launch groups the
+    // assignments and quantizes its rows by itself (writing h to its own buffer, since the
+    // w2 launch reads h while writing its terms into acc), the w2 GEMM launch quantizes h
+    // by itself, then the per-token sum.  Measured on MI355X to save the two small
+    // launches' time at one to four tokens; the same bits as the sequence below.
     e = moe::launch_grouped_gemm_swiglu_grouping(a_expert, a_src, a_dst, a_w, R, E, S, T, x,
                                                  w.offsets, w.row_src, w.row_dst, w.row_w,
                                                  w.tok_off, w.tok_rows, w.err,
                                                  (const uint8_t*)L->w13_packed, I, H, L->g_gate,
                                                  L->g_up, w.h16, stream, false);
     if (e != hipSuccess) return hip_status(e, "layer: grouping w13 GEMM + SwiGLU launch");
-  } else {
-    // grouping + NVFP4 quantization of the S source rows (one launch); the w13 GEMM reads
-    // grouped row i from source row row_src[i], so no gathered copy of x is made
-    e = moe::launch_group_quantize(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
-                                   w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, x, H, w.xq,
-                                   w.xs, w.xgs, stream);
-    if (e != hipSuccess) return hip_status(e, "layer: group+quantize launch");
+    e = moe::launch_grouped_gemm_quantizing(w.h16, w.offsets, E, R, (const uint8_t*)L->w2_packed, H,
+                                            I, w.acc, w.row_w, L->g_down, stream);
+    if (e != hipSuccess) return hip_status(e, "layer: quantizing w2 GEMM launch");
+    e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
+    return hip_status(e, "layer: scatter launch");
   }
-  if (fused_grouping) {
-    // (w13 with the SwiGLU epilogue ran in the grouping launch; h is quantized by the w2 one)
-  } else if (all_mfma) {
+  // grouping + NVFP4 quantization of the S source rows (one launch); the w13 GEMM reads
+  // grouped row i from source row row_src[i], so no gathered copy of x is made
+  e = moe::launch_group_quantize(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
+                                 w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, x, H, w.xq,
+                                 w.xs, w.xgs, stream);
+  if (e != hipSuccess) return hip_status(e, "layer: group+quantize launch");
+  if (all_mfma) {
     // SwiGLU in the w13 GEMM's epilogue (h in bf16 instead of the fp32 gate|up products),
     // then the NVFP4 quantization of h; the same bits as the unfused sequence below
     uint16_t* h = (uint16_t*)w.acc;
@@ -341,13 +342,8 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
     if (e != hipSuccess) return hip_status(e, "layer: swiglu+quantize launch");
   }
   // w2 GEMM writing each grouped row's scatter term (row_w * g_down * hgs * y), then a
-  // per-token sum over the token lists: the bits of moe_scatter_add on y.  A decode-sized
-  // batch quantizes h inside the w2 launch (one launch fewer).
-  if (fused_grouping) {
-    e = moe::launch_grouped_gemm_quantizing(w.h16, w.offsets, E, R, (const uint8_t*)L->w2_packed, H,
-                                            I, w.acc, w.row_w, L->g_down, stream);
-    if (e != hipSuccess) return hip_status(e, "layer: quantizing w2 GEMM launch");
-  } else if (R > 0) {
+  // per-token sum over the token lists: the bits of moe_scatter_add on y
+  if (R > 0) {
     e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, R, w.offsets, E, R,
                                  (const uint8_t*)L->w2_packed, H, I, w.acc, L->flags,
                                  L->gemv_max_rows, stream, w.row_w, L->g_down, w.hgs);

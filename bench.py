@@ -425,8 +425,9 @@ def w4a16_leg(args, weights):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode "
-              "(see the sharding notes in DESIGN.md); got --gpus %d" % args.gpus, file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this path has no multi-GPU mode (it would "
+              "shard by expert, each GPU running this layer on its share); got --gpus %d"
+              % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

@@ -15,8 +15,8 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def lib():
-    """The HIP library binding.  On a GPU machine a missing or stale library is an error,
-    never a skip: the product path has no fallback."""
+    """The HIP library binding.  On a machine with a GPU a missing or stale library is an
+    error, never a skip: the product path has no fallback."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")

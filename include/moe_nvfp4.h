@@ -96,8 +96,8 @@ int nvfp4_unpack_weights(const void* packed, int E, int N, int K,
 /* ----------------------------------------------------------------------------------
  * moe_gather_rows — group assignments by expert and gather their activation rows.
  * Source: [GG], section "What changed": one row per (stream, expert) is
- * gathered, and rows are grouped by expert id across the batch in ascending id order
- * (an ordered map), so group order depends only on which experts fired.
+ * gathered, and the batch's rows are grouped per expert in ascending expert id (the
+ * pages use an ordered map), so the group order is set by which experts received rows.
  *
  * Inputs:  x [S, H] bf16; assignment j = (a_expert[j], a_src[j], a_dst[j], a_w[j]),
  *          j < R: row a_src[j] of x goes to expert a_expert[j]; its result is added to
@@ -234,7 +234,9 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
  * x [S, H] bf16, assignments as for moe_gather_rows, out [T, H] bf16.
  * workspace: >= moe_layer_workspace_bytes(L, S, R, T) bytes, 256-byte aligned.  Its
  *   first int32 is the device error word (pass the workspace to moe_get_device_error).
- * Limits: H % 128 == 0, I % 128 == 0, H and I <= 8192, plus those of the steps.
+ * Limits: H % 128 == 0, I % 128 == 0, H and I <= 8192, max(S, R) * H < 2^31 and
+ * R * I < 2^31 (the NVFP4 rows a GEMM stages are addressed with 32-bit offsets), plus
+ * those of the steps.
  * ---------------------------------------------------------------------------------- */
 typedef struct {
   int E, H, I;

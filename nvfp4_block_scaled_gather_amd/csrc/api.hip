@@ -260,8 +260,12 @@ int check_layer(const moe_layer_desc* L, int S, int R, int T) {
   REQUIRE(L->I > 0 && L->I % 128 == 0 && L->I <= kMaxRowK, MOE_EUNSUPPORTED,
           "layer: I=%d must be a multiple of 128 in (0, %d]", L->I, kMaxRowK);
   REQUIRE(L->E + T <= kMaxGroupKeys, MOE_EUNSUPPORTED, "layer: E + T exceeds %d", kMaxGroupKeys);
+  // buffer ranges and offsets of the GEMMs' activation staging are 32-bit: the NVFP4 rows
+  // of x (S or R of them, H/2 bytes each) and of h (R rows of I/2 bytes) stay below 2 GiB
   REQUIRE((long long)(S > R ? S : R) * L->H < (1ll << 31), MOE_EUNSUPPORTED,
           "layer: activations exceed 2 GiB of NVFP4 rows");
+  REQUIRE((long long)R * L->I < (1ll << 31), MOE_EUNSUPPORTED,
+          "layer: %d rows of h (I=%d) exceed 2 GiB of NVFP4 rows", R, L->I);
   return MOE_OK;
 }
 }  // namespace

@@ -14,9 +14,9 @@ expert a_expert[j]; its result lands in output row a_dst[j] with router weight a
 
 Weights are canonical NVFP4 per expert: nibbles [N, K/2] (even element in the low
 nibble) and e4m3 scales [N, K/16].  w13 has N = 2I rows: rows [0, I) are the gate
-projection and rows [I, 2I) the up projection, back to back ([GG] "The seam CUTLASS
-forced open": gate_packed and up_packed sit back to back and double as the fused
-operand).  w2 has N = H rows and K = I.
+projection and rows [I, 2I) the up projection ([GG] "The seam CUTLASS forced open": the
+gate matrix followed by the up matrix is itself the fused w13 operand).  w2 has N = H rows
+and K = I.
 """
 import numpy as np
 
@@ -28,9 +28,10 @@ ERR_DST = 4      # a_dst[j] outside [0, T)
 
 
 def group_rows(a_expert, a_src, a_dst, a_w, E, S, T):
-    """Group assignments by expert id, ascending ([GG] "What changed": rows are grouped by
-    expert id across the batch with an ordered map, so group order is a pure function of
-    which experts fired).  Within an expert, rows keep their assignment order.
+    """Group assignments by expert id, ascending ([GG] "What changed": the batch's rows are
+    collected per expert in an ordered map, so the groups come out in ascending expert id
+    and their order depends on nothing but the set of experts that received rows).  Within
+    an expert, rows keep their assignment order.
 
     Assignments with an out-of-range expert, source or destination are dropped; their
     error bits are OR-ed into ``err``.  Dropped rows occupy the tail i >= offsets[E]

@@ -119,6 +119,15 @@ def test_argument_errors_are_reported_before_launch(lib):
                                  need, null) == B.MOE_EUNSUPPORTED
     assert lib.moe_layer_forward(None, p16, 4, p16, p16, p16, p16, 8, 4, p16, ws, need, null) == B.MOE_EINVAL
     assert lib.moe_get_device_error(null, null) == B.MOE_EINVAL
+    # h's NVFP4 rows (R x I/2 bytes) beyond the GEMM's 32-bit staging range, while x's rows
+    # (R x H/2) are not: refused before any launch instead of wrapping the offsets
+    narrow = B.MoeLayerDesc(8, 128, 8192, 4096, 4096, 4096, 4096, 4096, 0, 0)
+    R_big = 600000
+    assert R_big * 128 < (1 << 31) <= R_big * 8192
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(narrow), 4, R_big, 4) == 0
+    assert lib.moe_layer_forward(ctypes.byref(narrow), p16, 4, p16, p16, p16, p16, R_big, 4, p16,
+                                 ws, 1 << 40, null) == B.MOE_EUNSUPPORTED
+    assert b"rows of h" in lib.moe_last_error()
     # W4A16: K beyond what the staged bf16 rows fit in LDS, misalignment, H above 4096
     assert lib.grouped_gemm_w4a16(p16, p16, 8, 4, p16, 64, 8192, p16, null) == B.MOE_EUNSUPPORTED
     assert lib.grouped_gemm_w4a16(p16, p16, 8, 4, p16, 64, 100, p16, null) == B.MOE_EUNSUPPORTED

@@ -372,3 +372,127 @@ def test_w4a16_layer_batch_parity_and_determinism():
     for t in (1, 4):
         alone = _run_w4a16(d, np.arange(t * k, t * k + k))
         assert np.array_equal(alone[t], full[t])
+
+
+# --------------------------------------------------------------------------- W4A4 layer
+def _w4a4_term_closed_form(x_row_bits, w13, w2, gg, gu, gd, rw, I, H):
+    """One assignment's scatter term and its row globals, written out from the steps of
+    [GG] "What changed" with the pinned quantizer, exact rational GEMMs and the logistic
+    function in float64 (no other oracle code):
+      xq, xs, gx = quantize(x);  ag[j], au[j] = exact sums of x_deq * w13_deq over k
+      h = bf16( silu(gx * gg * ag) * (gx * gu * au) )       (per-half globals, option (a))
+      hq, hs, gh = quantize(h);  y[n] = exact sum of h_deq * w2_deq over j
+      term = rw * gd * gh * y                                (exact rational)"""
+    xq, xs, gx = nvfp4.quantize_row(nvfp4.bf16_bits_to_f32(x_row_bits))
+    xv = [_val(xq, xs, k) for k in range(H)]
+    ag = [sum(xv[k] * _val(w13[0][j], w13[1][j], k) for k in range(H)) for j in range(I)]
+    au = [sum(xv[k] * _val(w13[0][I + j], w13[1][I + j], k) for k in range(H))
+          for j in range(I)]
+    zg = [float(Fraction(float(gx)) * Fraction(float(gg)) * a) for a in ag]
+    zu = [float(Fraction(float(gx)) * Fraction(float(gu)) * a) for a in au]
+    h = nvfp4.f64_to_bf16_bits(np.array([g / (1.0 + np.exp(-g)) * u for g, u in zip(zg, zu)]))
+    hq, hs, gh = nvfp4.quantize_row(nvfp4.bf16_bits_to_f32(h))
+    hv = [_val(hq, hs, j) for j in range(I)]
+    y = [sum(hv[j] * _val(w2[0][n], w2[1][n], j) for j in range(I)) for n in range(H)]
+    c = Fraction(float(rw)) * Fraction(float(gd)) * Fraction(float(gh))
+    return [c * v for v in y], float(gx), float(gh)
+
+
+def _w4a4_case():
+    """Three experts, two tokens: token 0 takes experts 2 and 0 (assignment order differs
+    from the grouped order), token 1 expert 2 alone; gate, up and down globals differ."""
+    rng = np.random.default_rng(36)
+    E, H, I = 3, 32, 16
+    x = _bf16_rows(rng, 2, H, -2, 2)
+    # weight scales 2^-4 .. 2^-2: the SwiGLU inputs come out of order one, where silu is
+    # far from both of its linear limits (a swapped pair of globals would cancel there)
+    W13 = [_rand_nvfp4(rng, 2 * I, H, 0x18, 0x28) for _ in range(E)]
+    W2 = [_rand_nvfp4(rng, H, I, 0x18, 0x28) for _ in range(E)]
+    g = (np.array([0.5, 1.25, 0.75], np.float32), np.array([0.25, 1.5, 0.375], np.float32),
+         np.array([0.125, 2.0, 0.5], np.float32))
+    a = dict(a_expert=np.array([2, 0, 2]), a_src=np.array([0, 0, 1]),
+             a_dst=np.array([0, 0, 1]), a_w=np.array([0.5, 0.25, 0.75], np.float32))
+    return dict(x=x, W13=W13, W2=W2, g=g, E=E, H=H, I=I, T=2, **a)
+
+
+def _w4a4_closed_form(d):
+    T, H, I = d["T"], d["H"], d["I"]
+    gg, gu, gd = d["g"]
+    sums = [[Fraction(0)] * H for _ in range(T)]
+    gxs, ghs = [], []
+    for j in range(len(d["a_expert"])):
+        e, s, t = int(d["a_expert"][j]), int(d["a_src"][j]), int(d["a_dst"][j])
+        term, gx, gh = _w4a4_term_closed_form(d["x"][s], d["W13"][e], d["W2"][e], gg[e], gu[e],
+                                              gd[e], d["a_w"][j], I, H)
+        sums[t] = [a + b for a, b in zip(sums[t], term)]
+        gxs.append(gx)
+        ghs.append(gh)
+    out = nvfp4.f64_to_bf16_bits(np.array([[float(v) for v in row] for row in sums]))
+    return out, gxs, ghs
+
+
+def _w4a4_oracle(d, sel=None):
+    idx = np.arange(len(d["a_expert"])) if sel is None else np.asarray(sel)
+    return moe.layer_forward(d["x"], d["a_expert"][idx], d["a_src"][idx], d["a_dst"][idx],
+                             d["a_w"][idx], d["T"], lambda e: d["W13"][e], lambda e: d["W2"][e],
+                             *d["g"], d["E"], d["H"], d["I"])
+
+
+def test_w4a4_layer_single_row_closed_form():
+    """[GG] "What changed": one token routed to one expert; the oracle's layer equals the
+    closed form bit for bit, and the case separates the two row globals and the two
+    halves' globals (so a swapped or dropped global would change the result)."""
+    d = _w4a4_case()
+    one = {**d, "a_expert": d["a_expert"][2:], "a_src": d["a_src"][2:],
+           "a_dst": np.array([0]), "a_w": d["a_w"][2:], "T": 1}
+    want, gxs, ghs = _w4a4_closed_form(one)
+    assert gxs[0] != ghs[0] and gxs[0] != 1.0 and ghs[0] != 1.0
+    got = _w4a4_oracle(one)
+    assert np.array_equal(got, want)
+    assert np.count_nonzero(got) > 0.9 * got.size
+
+
+def test_w4a4_layer_multi_row_closed_form():
+    """Two assignments of one token in the opposite of their grouped order, plus a second
+    token: the oracle's grouping, router-weight permutation and per-token sum match the
+    closed form (exact sum of the terms, rounded once to bf16)."""
+    d = _w4a4_case()
+    want, _, _ = _w4a4_closed_form(d)
+    assert np.array_equal(_w4a4_oracle(d), want)
+
+
+@pytest.mark.parametrize("mistake", ["swap_half_globals", "drop_x_global", "drop_h_global",
+                                     "x_global_in_scatter", "weights_unpermuted"])
+def test_w4a4_layer_closed_form_catches_wiring_mistakes(monkeypatch, mistake):
+    """Plants each plausible wiring mistake in the oracle's layer (on the CPU) and checks
+    that the closed-form pin above then fails: the pin constrains every global's place."""
+    d = _w4a4_case()
+    want, _, _ = _w4a4_closed_form(d)
+    seen = {}
+    swiglu, scatter, group = moe.swiglu, moe.scatter_add, moe.group_rows
+
+    def bad_swiglu(acc13, offsets, g_gate, g_up, row_gs, I):
+        seen["xgs"] = np.array(row_gs)
+        if mistake == "swap_half_globals":
+            g_gate, g_up = g_up, g_gate
+        if mistake == "drop_x_global":
+            row_gs = np.ones_like(row_gs)
+        return swiglu(acc13, offsets, g_gate, g_up, row_gs, I)
+
+    def bad_scatter(y, offsets, row_w, g_down, row_gs, tok_off, tok_rows, T):
+        if mistake == "drop_h_global":
+            row_gs = np.ones_like(row_gs)
+        if mistake == "x_global_in_scatter":
+            row_gs = seen["xgs"]
+        return scatter(y, offsets, row_w, g_down, row_gs, tok_off, tok_rows, T)
+
+    def bad_group(*args):
+        g = group(*args)
+        if mistake == "weights_unpermuted":
+            g["row_w"] = np.asarray(args[3], np.float32).copy()
+        return g
+
+    monkeypatch.setattr(moe, "swiglu", bad_swiglu)
+    monkeypatch.setattr(moe, "scatter_add", bad_scatter)
+    monkeypatch.setattr(moe, "group_rows", bad_group)
+    assert not np.array_equal(_w4a4_oracle(d), want)

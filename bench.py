@@ -5,8 +5,8 @@ A step is one moe_layer_forward call over one synthetic batch: grouping, gather 
 quantize, w13 grouped GEMM, SwiGLU + re-quantize, w2 grouped GEMM, scatter-add — every
 step of the path, inputs and packed weights already resident in HBM.  The step is timed
 both as eager launches and as one HIP-graph replay of the same launches (the pages'
-graph-launched layer); the graph time is the reported value, and the run checks that a
-replay gives the eager output bit for bit.  Each timed block follows an untimed warm-up of
+graph-launched layer); the faster of the two medians is the reported value (both are in
+the line), and the run checks that a replay gives the eager output bit for bit.  Each timed block follows an untimed warm-up of
 at least --warmup steps and at least --settle-ms of continuous work (default 500 ms;
 measured on MI355X, the layer runs up to 10% slower during the first few hundred ms of
 work after the GPU was idle).
@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer ms + weight-stream HBM GB/s (% of peak), 288 experts, 570/2303 rows"
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 W13_BYTES_PER_EXPERT = 2 * 2048 * 4096 * 9 // 16   # 9,437,184
+W2_BYTES_PER_EXPERT = 2048 * 4096 * 9 // 16      # 4,718,592
 LAYER_BYTES_PER_EXPERT = 3 * 2048 * 4096 * 9 // 16  # 14,155,776
 
 
@@ -71,6 +72,8 @@ def parse():
     p.add_argument("--gemv-max-rows", type=int, default=None)
     p.add_argument("--kernel-iters", type=int, default=30)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-read-probe", action="store_true",
+                   help="skip the measured read roofline (moe_hbm_read_probe over 4.0 GiB)")
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches only (default: also a HIP-graph replay of the "
                         "layer, which is the reported value)")
@@ -171,9 +174,11 @@ def time_graph(dl, steps, warmup, settle_ms=0.0):
     return float(np.median(per)), float(np.min(per)), float(np.max(per)), graph
 
 
-def time_w13(dl, iters, settle_ms=0.0):
-    """Average duration of one w13 grouped-GEMM launch (grouped_gemm_nvfp4) on the layer's
-    own quantized activations, HIP events on the launch stream."""
+def time_gemms(dl, iters, settle_ms=0.0):
+    """Average duration of one w13 and one w2 grouped-GEMM launch (grouped_gemm_nvfp4) on
+    the layer's own data: the quantized activation rows for w13, and the quantized SwiGLU
+    output of those rows for w2 (the plain fp32 output, without the layer's scatter-ready
+    epilogue).  HIP events on the launch stream, back-to-back launches."""
     import torch
     from nvfp4_block_scaled_gather_amd import binding as B
     wl = dl.wl
@@ -184,24 +189,79 @@ def time_w13(dl, iters, settle_ms=0.0):
     rs, rd, rw = e((R,), torch.int32), e((R,), torch.int32), e((R,), torch.float32)
     to, tr, err = e((T + 1,), torch.int32), e((R,), torch.int32), e((1,), torch.int32)
     stream = torch.cuda.Stream()
+    flags, gmax = dl.desc.flags, dl.desc.gemv_max_rows
+
+    def timed(launch):
+        # untimed: at least 10 launches and settle_ms of them, to steady clocks
+        warm(launch, 10, settle_ms)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(iters):
+            launch()
+        stop.record(stream)
+        stop.synchronize()
+        return start.elapsed_time(stop) / iters
+
     with torch.cuda.stream(stream):
         B.moe_gather_rows(dl.x, S, H, dl.a_expert, dl.a_src, dl.a_dst, dl.a_w, R, E, T, xg, off,
                           rs, rd, rw, to, tr, err)
         xq, xs, xgs = e((R, H // 2), torch.uint8), e((R, H // 16), torch.uint8), e((R,), torch.float32)
         B.nvfp4_quantize_rows(xg, R, H, xq, xs, xgs)
         acc = e((R, 2 * I), torch.float32)
-        flags, gmax = dl.desc.flags, dl.desc.gemv_max_rows
-        # untimed: at least 10 launches and settle_ms of them, to steady clocks
-        warm(lambda: B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gmax),
-             10, settle_ms)
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(iters):
-            B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gmax)
-        stop.record(stream)
-    stop.synchronize()
-    return start.elapsed_time(stop) / iters
+        w13_ms = timed(lambda: B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc,
+                                                    flags, gmax))
+        h = e((R, I), torch.int16)
+        B.swiglu_grouped(acc, R, I, off, E, dl.g_gate, dl.g_up, xgs, h)
+        hq, hs, hgs = e((R, I // 2), torch.uint8), e((R, I // 16), torch.uint8), e((R,), torch.float32)
+        B.nvfp4_quantize_rows(h, R, I, hq, hs, hgs)
+        y = e((R, H), torch.float32)
+        w2_ms = timed(lambda: B.grouped_gemm_nvfp4(hq, hs, off, E, R, dl.w2, H, I, y, flags, gmax))
+    torch.cuda.synchronize()
+    return w13_ms, w2_ms
+
+
+# Read-probe buffer: 14,564 GEMM work items of 288 KiB (8 tiles of 36 KiB), 4.0 GiB
+READ_PROBE_BYTES = 14564 * 294912
+READ_PROBE_VARIANTS = {0: "contiguous per wave, 8 KiB in flight, 32 waves/CU",
+                       1: "contiguous per wave, 16 KiB in flight, 32 waves/CU",
+                       2: "contiguous per wave, 16 KiB in flight, 16 waves/CU",
+                       3: "the w13 GEMM's items: 4 waves x 2 tiles of 36 KiB, 4 KiB of each "
+                          "in flight"}
+
+
+def read_roofline(iters, settle_ms=0.0):
+    """The measured HBM read roofline: moe_hbm_read_probe over a 4.0 GiB buffer of random
+    bytes, each load pattern timed with HIP events on its launch stream over `iters`
+    back-to-back launches after a warm-up; GB/s = bytes read / average launch time."""
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12345)
+    buf = torch.randint(0, 256, (READ_PROBE_BYTES,), dtype=torch.uint8, device="cuda", generator=g)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    res = {}
+    with torch.cuda.stream(stream):
+        for v in range(B.moe_hbm_read_probe_variants()):
+            launch = lambda: B.moe_hbm_read_probe(buf, READ_PROBE_BYTES, v, 0x9E3779B9, sink)
+            warm(launch, 5, settle_ms)
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            for _ in range(iters):
+                launch()
+            stop.record(stream)
+            stop.synchronize()
+            ms = start.elapsed_time(stop) / iters
+            res[v] = {"pattern": READ_PROBE_VARIANTS.get(v, str(v)), "ms": ms,
+                      "GBps": READ_PROBE_BYTES / (ms * 1e-3) / 1e9}
+            log(json.dumps({"read_probe": v, **res[v]}))
+    del buf
+    torch.cuda.synchronize()
+    best = max(res, key=lambda v: res[v]["GBps"])
+    return {"GBps": res[best]["GBps"], "best_variant": best, "bytes": READ_PROBE_BYTES,
+            "variants": res}
 
 
 def cpu_baseline(wl, n_experts):
@@ -272,27 +332,33 @@ def run_workload(name, args, weights=None):
     torch.cuda.synchronize()
     launch = "eager"
     med, lo, hi = e_med, e_lo, e_hi
+    g_med = g_lo = g_hi = None
     if not args.no_graph:
-        med, lo, hi, graph = time_graph(dl, args.steps, args.warmup, args.settle_ms)
+        g_med, g_lo, g_hi, graph = time_graph(dl, args.steps, args.warmup, args.settle_ms)
         graph.replay()
         torch.cuda.synchronize()
         if not torch.equal(dl.out, eager_out):  # a replay must give the eager bits
             raise RuntimeError("graph replay output differs from the eager layer output")
-        launch = "hip-graph replay"
+        if g_med <= e_med:  # the faster launch mode is the reported one
+            med, lo, hi = g_med, g_lo, g_hi
+            launch = "hip-graph replay"
     n_act = len(wl.active_experts())
     wbytes = n_act * LAYER_BYTES_PER_EXPERT
-    w13_ms = time_w13(dl, args.kernel_iters, args.settle_ms)
+    w13_ms, w2_ms = time_gemms(dl, args.kernel_iters, args.settle_ms)
     res = {
         "workload": name, "expert_rows": wl.R, "tokens": wl.T, "active_experts": n_act,
         "launch": launch,
         "layer_ms_median": med, "layer_ms_min": lo, "layer_ms_max": hi,
         "layer_ms_eager_median": e_med, "layer_ms_eager_min": e_lo, "layer_ms_eager_max": e_hi,
         "layer_ms_eager_wall": wall,
+        "layer_ms_graph_median": g_med, "layer_ms_graph_min": g_lo, "layer_ms_graph_max": g_hi,
         "weight_bytes": wbytes, "weight_GBps": wbytes / (med * 1e-3) / 1e9,
         "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "frac_of_hbm_peak_eager": wbytes / (e_med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "w13_gemm_ms": w13_ms,
         "w13_GBps": n_act * W13_BYTES_PER_EXPERT / (w13_ms * 1e-3) / 1e9,
+        "w2_gemm_ms": w2_ms,
+        "w2_GBps": n_act * W2_BYTES_PER_EXPERT / (w2_ms * 1e-3) / 1e9,
         "gemm_path": {"flags": dl.desc.flags, "gemv_max_rows": dl.desc.gemv_max_rows},
     }
     log(json.dumps(res))
@@ -305,8 +371,9 @@ def decode_sweep(args, weights):
     Honest cache: before every timed call an untimed copy of --flush-mb MB (read and write)
     replaces the MALL and L2 contents, so the active experts' weights come from HBM (their
     113 MB at M=1 would otherwise fit in the 256 MB MALL).  Each call is a HIP-graph replay
-    (checked equal to the eager output) timed with HIP events; bytes per token are the
-    weight bytes streamed per step over M."""
+    (checked equal to the eager output) and, separately, eager calls, timed with HIP events;
+    the faster median is reported.  Bytes per token are the weight bytes streamed per step
+    over M."""
     import torch
     from nvfp4_block_scaled_gather_amd import layer as L
     from nvfp4_block_scaled_gather_amd import workloads as W
@@ -324,31 +391,38 @@ def decode_sweep(args, weights):
         if not torch.equal(dl.out, eager):
             raise RuntimeError("decode%d: graph replay differs from the eager output" % M)
 
-        def step():
-            dst.copy_(src)
-            graph.replay()
+        def timed(run):
+            def step():
+                dst.copy_(src)
+                run()
 
-        warm(step, args.warmup, args.settle_ms)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for a, b in ev:
-            dst.copy_(src)
-            a.record()
-            graph.replay()
-            b.record()
-        torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in ev)
-        med = float(np.median(t))
+            warm(step, args.warmup, args.settle_ms)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                dst.copy_(src)
+                a.record()
+                run()
+                b.record()
+            torch.cuda.synchronize()
+            return sorted(a.elapsed_time(b) for a, b in ev)
+
+        tg = timed(graph.replay)
+        te = timed(dl.forward)
+        g_med, e_med = float(np.median(tg)), float(np.median(te))
+        med, t, launch = (g_med, tg, "hip-graph replay") if g_med <= e_med else (e_med, te, "eager")
         n_act = len(wl.active_experts())
         wbytes = n_act * LAYER_BYTES_PER_EXPERT
         out.append({"M": M, "expert_rows": wl.R, "active_experts": n_act,
-                    "layer_us": med * 1e3, "layer_us_min": t[0] * 1e3,
+                    "layer_us": med * 1e3, "layer_us_min": t[0] * 1e3, "launch": launch,
+                    "layer_us_graph": g_med * 1e3, "layer_us_eager": e_med * 1e3,
                     "weight_bytes": wbytes, "weight_GBps": wbytes / (med * 1e-3) / 1e9,
                     "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                     "weight_bytes_per_token": wbytes / M, "tokens_per_s": M / (med * 1e-3)})
         log(json.dumps(out[-1]))
         del graph, dl
-    return {"launch": "hip-graph replay, %d MB cache flush before each call" % args.flush_mb,
+    return {"launch": "the faster of hip-graph replay and eager launches (both medians are "
+                      "given), %d MB cache flush before each call" % args.flush_mb,
             "points": out}
 
 
@@ -465,6 +539,12 @@ def main():
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(args.workload),
                 "kernel": "grouped_gemm_nvfp4 (w13, N=4096, K=4096) on %s" % args.workload,
                 "bytes_per_launch": alg_bytes}
+    if not args.no_read_probe:
+        log("measured read roofline")
+        rp = read_roofline(args.kernel_iters, args.settle_ms)
+        roofline["read_peak"] = rp
+        roofline["frac_of_read_peak"] = achieved / rp["GBps"]
+        roofline["read_peak_frac_of_spec"] = rp["GBps"] / HBM_PEAK_GBPS
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -484,8 +564,10 @@ def main():
         "layer_ms": ms, "layer_ms_min": res["layer_ms_min"], "layer_ms_max": res["layer_ms_max"],
         "frac_of_hbm_peak": res["frac_of_hbm_peak"],
         "layer_ms_eager": res["layer_ms_eager_median"],
+        "layer_ms_graph": res["layer_ms_graph_median"],
         "frac_of_hbm_peak_eager": res["frac_of_hbm_peak_eager"],
         "w13_gemm_ms": res["w13_gemm_ms"], "w13_weight_GBps": res["w13_GBps"],
+        "w2_gemm_ms": res["w2_gemm_ms"], "w2_weight_GBps": res["w2_GBps"],
         "roofline": roofline, "cpu_baseline": cpu, "also": also, "decode_sweep": sweep,
         "w4a16": w4a16,
         "host": platform.node(),

@@ -274,6 +274,26 @@ int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
                             const float* a_w, int R, int T, uint16_t* out,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ----------------------------------------------------------------------------------
+ * moe_hbm_read_probe — a measurement aid, not a step of the layer: reads `bytes` bytes
+ * at `src` once, with non-temporal 16-byte loads per lane, so that the time of the launch
+ * gives the HBM read bandwidth this GPU actually reaches — the measured read roofline the
+ * weight-streaming GEMMs are judged against ([MF], table "Bytes decide it before the
+ * kernel runs": the pages' layer roofline comes from a measured read bandwidth, below the
+ * spec; section "Next": profile the w13 GEMM against a raw read of the same access
+ * pattern).
+ * variant (0 <= variant < moe_hbm_read_probe_variants()): 0, 1, 2: each wave streams a
+ *   contiguous run with 8, 16 or 16 KiB of loads in flight, 32, 32 or 16 waves per CU;
+ *   3: the w13 GEMM's pattern: one workgroup of 4 waves per 288 KiB item of 8 tiles of
+ *   36 KiB, each wave walking two tiles side by side with 4 KiB of each in flight.
+ * bytes: a positive multiple of 294,912 (one such item); src 16-byte aligned.
+ * sink: one device uint32, written only if a lane's XOR of the data it read equals `key`
+ *   (it keeps the loads alive; its value means nothing).
+ * ---------------------------------------------------------------------------------- */
+int moe_hbm_read_probe(const void* src, size_t bytes, int variant, uint32_t key,
+                       uint32_t* sink, hipStream_t stream);
+int moe_hbm_read_probe_variants(void);
+
 /* Synchronizes `stream`, then returns the device error word at `err_word` (the
  * err_word of moe_gather_rows, or a moe_layer_forward workspace), or a negative
  * moe_status if the read fails. */

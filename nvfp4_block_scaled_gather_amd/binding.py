@@ -62,6 +62,8 @@ _SIGNATURES = {
                                _P, _P, ctypes.c_size_t, _P]),
     "moe_layer_forward_w4a16": (_I, [ctypes.POINTER(MoeLayerDesc), _P, _I, _P, _P, _P, _P, _I,
                                      _I, _P, _P, ctypes.c_size_t, _P]),
+    "moe_hbm_read_probe": (_I, [_P, ctypes.c_size_t, _I, ctypes.c_uint32, _P, _P]),
+    "moe_hbm_read_probe_variants": (_I, []),
     "moe_get_device_error": (_I, [_P, _P]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_source_hash": (ctypes.c_char_p, []),
@@ -185,6 +187,15 @@ def moe_layer_forward_w4a16(desc, x, S, a_expert, a_src, a_dst, a_w, R, T, out, 
     _check("moe_layer_forward_w4a16", load().moe_layer_forward_w4a16(
         ctypes.byref(desc), _ptr(x), S, _ptr(a_expert), _ptr(a_src), _ptr(a_dst), _ptr(a_w), R, T,
         _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def moe_hbm_read_probe(src, nbytes, variant, key, sink, stream=None):
+    _check("moe_hbm_read_probe", load().moe_hbm_read_probe(
+        _ptr(src), nbytes, variant, key, _ptr(sink), _stream(stream)))
+
+
+def moe_hbm_read_probe_variants():
+    return int(load().moe_hbm_read_probe_variants())
 
 
 def moe_get_device_error(err_word, stream=None):

@@ -7,6 +7,13 @@
 
 #include "common.h"
 
+namespace moe {
+// HBM read probe (k_probe.hip): bytes a multiple of 294,912, variant in [0, probe_variants()).
+int probe_variants();
+hipError_t launch_read_probe(const uint8_t* src, size_t bytes, int variant, uint32_t key,
+                             uint32_t* sink, hipStream_t s);
+}  // namespace moe
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -42,6 +49,7 @@ constexpr int kMaxGroupKeys = 16000;  // E + T, LDS histograms of the grouping k
 constexpr int kMaxRowK = 8192;        // row kernels keep a row in registers
 constexpr int kMaxE = 8192;
 constexpr int kMaxBf16K = 4096;       // W4A16: 16 staged bf16 rows of K must fit in LDS
+constexpr size_t kProbeUnit = 294912; // read probe: one GEMM work item (8 tiles of 36 KiB)
 
 int check_group_args(const void* a_expert, const void* a_src, const void* a_dst, const void* a_w,
                      int R, int E, int S, int T, const void* expert_offsets, const void* row_src,
@@ -275,17 +283,17 @@ size_t moe_layer_workspace_bytes(const moe_layer_desc* L, int S, int R, int T) {
   return carve(L, S, R, T, nullptr).bytes;
 }
 
-int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* a_expert,
-                      const int32_t* a_src, const int32_t* a_dst, const float* a_w, int R, int T,
-                      uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// Arguments of moe_layer_forward other than the workspace.
+int check_layer_call(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* a_expert,
+                     const int32_t* a_src, const int32_t* a_dst, const float* a_w, int R, int T,
+                     const uint16_t* out) {
   int st = check_layer(L, S, R, T);
   if (st != MOE_OK) return st;
   REQUIRE(L->w13_packed && L->w2_packed && L->g_gate && L->g_up && L->g_down, MOE_EINVAL,
           "layer: null weights / globals");
-  REQUIRE(workspace && aligned(workspace, 256), MOE_EINVAL, "layer: workspace null or not 256-byte aligned");
-  const LayerWs w = carve(L, S, R, T, (uint8_t*)workspace);
-  REQUIRE(workspace_bytes >= w.bytes, MOE_EWORKSPACE, "layer: workspace %zu bytes < %zu needed",
-          workspace_bytes, w.bytes);
   if (R > 0) REQUIRE(a_expert && a_src && a_dst && a_w, MOE_EINVAL, "layer: null assignment array");
   if (R > 0 && S > 0) REQUIRE(x, MOE_EINVAL, "layer: null x");
   if (T > 0) REQUIRE(out, MOE_EINVAL, "layer: null out");
@@ -294,6 +302,13 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
   REQUIRE(L->flags == MOE_PATH_AUTO || L->flags == MOE_PATH_FORCE_GEMV || L->flags == MOE_PATH_FORCE_MFMA,
           MOE_EINVAL, "layer: unknown flags %d", L->flags);
   REQUIRE(L->gemv_max_rows >= 0, MOE_EINVAL, "layer: gemv_max_rows < 0");
+  return MOE_OK;
+}
+
+// The launches of one layer call over the carved workspace w (arguments already checked).
+int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* a_expert,
+              const int32_t* a_src, const int32_t* a_dst, const float* a_w, int R, int T,
+              uint16_t* out, const LayerWs& w, hipStream_t stream) {
   const int E = L->E, H = L->H, I = L->I;
   hipError_t e;
   const bool all_mfma = L->flags == MOE_PATH_FORCE_MFMA ||
@@ -356,6 +371,21 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
   e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
   return hip_status(e, "layer: scatter launch");
 }
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* a_expert,
+                      const int32_t* a_src, const int32_t* a_dst, const float* a_w, int R, int T,
+                      uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_layer_call(L, x, S, a_expert, a_src, a_dst, a_w, R, T, out);
+  if (st != MOE_OK) return st;
+  REQUIRE(workspace && aligned(workspace, 256), MOE_EINVAL, "layer: workspace null or not 256-byte aligned");
+  const LayerWs w = carve(L, S, R, T, (uint8_t*)workspace);
+  REQUIRE(workspace_bytes >= w.bytes, MOE_EWORKSPACE, "layer: workspace %zu bytes < %zu needed",
+          workspace_bytes, w.bytes);
+  return run_layer(L, x, S, a_expert, a_src, a_dst, a_w, R, T, out, w, stream);
+}
 
 int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
                             const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
@@ -409,6 +439,22 @@ int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
   e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
   return hip_status(e, "layer: scatter launch");
 }
+
+int moe_hbm_read_probe(const void* src, size_t bytes, int variant, uint32_t key, uint32_t* sink,
+                       hipStream_t stream) {
+  REQUIRE(variant >= 0 && variant < moe::probe_variants(), MOE_EINVAL,
+          "read probe: variant %d outside [0, %d)", variant, moe::probe_variants());
+  REQUIRE(bytes > 0 && bytes % kProbeUnit == 0, MOE_EUNSUPPORTED,
+          "read probe: %zu bytes is not a positive multiple of %zu", bytes, kProbeUnit);
+  REQUIRE(bytes / kProbeUnit < (1u << 31), MOE_EUNSUPPORTED, "read probe: %zu bytes is too large",
+          bytes);
+  REQUIRE(src && sink, MOE_EINVAL, "read probe: null pointer");
+  REQUIRE(aligned(src, 16) && aligned(sink, 4), MOE_EINVAL, "read probe: src not 16-byte aligned");
+  return hip_status(moe::launch_read_probe((const uint8_t*)src, bytes, variant, key, sink, stream),
+                    "read probe launch");
+}
+
+int moe_hbm_read_probe_variants(void) { return moe::probe_variants(); }
 
 int moe_get_device_error(const void* err_word, hipStream_t stream) {
   REQUIRE(err_word, MOE_EINVAL, "null error word");

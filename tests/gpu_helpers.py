@@ -64,3 +64,32 @@ def run_gemm(binding, aq, as_, offsets, wp, N, K, flags, gemv_max=4):
     binding.grouped_gemm_nvfp4(dev(aq), dev(as_), dev(offsets), E, R, wp, N, K, out, flags, gemv_max)
     sync()
     return host(out)[:R]
+
+
+def composed_layer(B, dl, flags, gemv_max):
+    """The layer's steps as separate ABI calls (gather, quantize, w13 GEMM, SwiGLU,
+    quantize, w2 GEMM, scatter-add), on the layer's resident inputs; returns out [T, H]."""
+    import torch
+    wl = dl.wl
+    R, E, H, I, T, S = wl.R, wl.E, wl.H, wl.I, wl.T, wl.S
+    i32, f32, u8, i16 = torch.int32, torch.float32, torch.uint8, torch.int16
+    xg = empty((R, H), i16)
+    off = empty((E + 1,), i32)
+    rs, rd, rw = empty((R,), i32), empty((R,), i32), empty((R,), f32)
+    to, tr, err = empty((T + 1,), i32), empty((R,), i32), empty((1,), i32)
+    B.moe_gather_rows(dl.x, S, H, dl.a_expert, dl.a_src, dl.a_dst, dl.a_w, R, E, T, xg, off, rs,
+                      rd, rw, to, tr, err)
+    xq, xs, xgs = empty((R, H // 2), u8), empty((R, H // 16), u8), empty((R,), f32)
+    B.nvfp4_quantize_rows(xg, R, H, xq, xs, xgs)
+    acc = empty((R, 2 * I), f32)
+    B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gemv_max)
+    h = empty((R, I), i16)
+    B.swiglu_grouped(acc, R, I, off, E, dl.g_gate, dl.g_up, xgs, h)
+    hq, hs, hgs = empty((R, I // 2), u8), empty((R, I // 16), u8), empty((R,), f32)
+    B.nvfp4_quantize_rows(h, R, I, hq, hs, hgs)
+    y = empty((R, H), f32)
+    B.grouped_gemm_nvfp4(hq, hs, off, E, R, dl.w2, H, I, y, flags, gemv_max)
+    out = empty((T, H), i16)
+    B.moe_scatter_add(y, R, H, off, E, rw, dl.g_down, hgs, to, tr, T, out)
+    sync()
+    return host(out)

@@ -141,6 +141,19 @@ def test_argument_errors_are_reported_before_launch(lib):
                                        need - 1, null) == B.MOE_EWORKSPACE
 
 
+def test_read_probe_rejects_bad_arguments_before_launch(lib):
+    p16 = ctypes.c_void_p(4096)
+    n = lib.moe_hbm_read_probe_variants()
+    assert n == 4
+    unit = 294912
+    assert lib.moe_hbm_read_probe(p16, unit + 16, 0, 0, p16, None) == B.MOE_EUNSUPPORTED
+    assert lib.moe_hbm_read_probe(p16, 0, 0, 0, p16, None) == B.MOE_EUNSUPPORTED
+    assert lib.moe_hbm_read_probe(p16, unit, n, 0, p16, None) == B.MOE_EINVAL
+    assert lib.moe_hbm_read_probe(p16, unit, -1, 0, p16, None) == B.MOE_EINVAL
+    assert lib.moe_hbm_read_probe(None, unit, 0, 0, p16, None) == B.MOE_EINVAL
+    assert lib.moe_hbm_read_probe(ctypes.c_void_p(4104), unit, 0, 0, p16, None) == B.MOE_EINVAL
+
+
 def test_workspace_grows_with_rows(lib):
     d = B.MoeLayerDesc(288, 4096, 2048, 4096, 4096, 4096, 4096, 4096, 0, 4)
     a = lib.moe_layer_workspace_bytes(ctypes.byref(d), 570, 570, 8)

@@ -530,3 +530,28 @@ def test_scatter_within_bf16_rounding(lib):
     scale = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True)) + 1e-30
     assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-5 * scale)
     assert not got[T - 1].any()
+
+
+# ------------------------------------------------------------------------------ read probe
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_read_probe_reads_every_byte_it_is_given(lib, variant):
+    """moe_hbm_read_probe (the measured read roofline) reads the whole buffer: one 16-byte
+    word planted at the first, a middle and the last position is seen (the sink takes the
+    key only when some lane's XOR fold equals it), and nothing is written otherwise."""
+    import torch
+    from nvfp4_block_scaled_gather_amd import binding as B
+    unit = 294912
+    nbytes = 2 * unit
+    key = 0x12345678
+    for off in (0, nbytes // 2 + 1024 * 5 + 48, nbytes - 16):
+        say("read probe variant", variant, "offset", off)
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        word = torch.tensor([key, 0, 0, 0], dtype=torch.int64).to(torch.int32)
+        buf[off:off + 16] = word.view(torch.uint8).cuda()
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        B.moe_hbm_read_probe(buf, nbytes, variant, key + 1, sink)
+        sync()
+        assert int(sink.item()) == 0
+        B.moe_hbm_read_probe(buf, nbytes, variant, key, sink)
+        sync()
+        assert int(sink.item()) == key

@@ -15,7 +15,7 @@ import pytest
 from oracle import moe as omoe
 from oracle import nvfp4 as onv
 
-from gpu_helpers import dev, empty, host, say, sync
+from gpu_helpers import composed_layer, dev, empty, host, say, sync
 
 pytestmark = pytest.mark.gpu
 
@@ -64,34 +64,6 @@ def test_tiny_layer_matches_oracle(lib, tiny):
     assert frac >= E2E_FRAC
 
 
-def _composed(B, dl, flags, gemv_max):
-    """The layer's steps as separate ABI calls."""
-    import torch
-    wl = dl.wl
-    R, E, H, I, T, S = wl.R, wl.E, wl.H, wl.I, wl.T, wl.S
-    i32, f32, u8, i16 = torch.int32, torch.float32, torch.uint8, torch.int16
-    xg = empty((R, H), i16)
-    off = empty((E + 1,), i32)
-    rs, rd, rw = empty((R,), i32), empty((R,), i32), empty((R,), f32)
-    to, tr, err = empty((T + 1,), i32), empty((R,), i32), empty((1,), i32)
-    B.moe_gather_rows(dl.x, S, H, dl.a_expert, dl.a_src, dl.a_dst, dl.a_w, R, E, T, xg, off, rs,
-                      rd, rw, to, tr, err)
-    xq, xs, xgs = empty((R, H // 2), u8), empty((R, H // 16), u8), empty((R,), f32)
-    B.nvfp4_quantize_rows(xg, R, H, xq, xs, xgs)
-    acc = empty((R, 2 * I), f32)
-    B.grouped_gemm_nvfp4(xq, xs, off, E, R, dl.w13, 2 * I, H, acc, flags, gemv_max)
-    h = empty((R, I), i16)
-    B.swiglu_grouped(acc, R, I, off, E, dl.g_gate, dl.g_up, xgs, h)
-    hq, hs, hgs = empty((R, I // 2), u8), empty((R, I // 16), u8), empty((R,), f32)
-    B.nvfp4_quantize_rows(h, R, I, hq, hs, hgs)
-    y = empty((R, H), f32)
-    B.grouped_gemm_nvfp4(hq, hs, off, E, R, dl.w2, H, I, y, flags, gemv_max)
-    out = empty((T, H), i16)
-    B.moe_scatter_add(y, R, H, off, E, rw, dl.g_down, hgs, to, tr, T, out)
-    sync()
-    return host(out)
-
-
 @pytest.mark.parametrize("flags,gemv_max", [(0, 4), (1, 4), (2, 4), (0, 0)])
 def test_layer_equals_separate_calls(lib, flags, gemv_max):
     """The fused layer (gather inside quantize, quantize inside SwiGLU) is bit-identical
@@ -104,7 +76,7 @@ def test_layer_equals_separate_calls(lib, flags, gemv_max):
     dl = L.DeviceLayer(wl, flags=flags, gemv_max_rows=gemv_max)
     got = host(dl.forward())
     sync()
-    assert np.array_equal(got, _composed(B, dl, flags, gemv_max))
+    assert np.array_equal(got, composed_layer(B, dl, flags, gemv_max))
 
 
 @pytest.mark.parametrize("R,hot", [(1, 0), (17, 17), (32, 20), (33, 20)])
@@ -132,7 +104,7 @@ def test_decode_sized_layer_equals_separate_calls(lib, R, hot):
     sync()
     err = dl.device_error()
     assert err == (0 if R < 17 else B.MOE_ERR_EXPERT | B.MOE_ERR_DST), err
-    assert np.array_equal(got, _composed(B, dl, 0, 0))
+    assert np.array_equal(got, composed_layer(B, dl, 0, 0))
 
 
 @pytest.mark.parametrize("flags", [1, 2])
@@ -245,20 +217,6 @@ def test_layer_at_the_largest_hidden_size(lib):
 
 
 # ------------------------------------------------------------------------------ full size
-@pytest.fixture(scope="module")
-def full_weights():
-    """The 288-expert, H=4096, I=2048 NVFP4 expert set (4.08 GB), packed once."""
-    from nvfp4_block_scaled_gather_amd import layer as L
-    from nvfp4_block_scaled_gather_amd import workloads as W
-    say("packing the full expert set")
-    wl = W.make_workload("decode1")
-    w13 = L.pack_expert_weights(wl.w13, wl.E, 2 * wl.I, wl.H)
-    say("w13 packed")
-    w2 = L.pack_expert_weights(wl.w2, wl.E, wl.H, wl.I)
-    say("w2 packed")
-    return w13, w2
-
-
 def _pick_tokens(wl, name):
     counts = np.bincount(wl.a_dst, minlength=wl.T)
     if name == "decode1":

@@ -13,7 +13,8 @@
  * ---------------------------------------
  * - Pointers are DEVICE pointers unless the comment says "host".  bf16 values are passed
  *   as their uint16_t bit patterns.  The caller allocates and owns every buffer; the
- *   library allocates nothing, keeps no global state and is reentrant.
+ *   library allocates nothing and is reentrant.  Its one piece of global state is the
+ *   fixed scratch array of moe_layer_forward_noalloc (one per GPU).
  * - Every call is asynchronous on the given stream: it validates its arguments on the
  *   host, enqueues kernels and returns.  Only moe_get_device_error() synchronizes.
  * - Return value: MOE_OK (0) or a negative moe_status.  Argument errors (null pointers
@@ -254,6 +255,30 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S,
                       const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
                       const float* a_w, int R, int T, uint16_t* out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------------
+ * moe_layer_forward_noalloc — moe_layer_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same launches and bit-identical results, with the workspace taken from
+ * a fixed array the library holds on each GPU (MOE_NOALLOC_SCRATCH_BYTES, allocated with
+ * the library's code object on a GPU and held until the process ends) instead of a caller
+ * buffer.  It calls no allocating routine; its first call on a device looks up that
+ * device's array address once (hipGetSymbolAddress).
+ * Same arguments as moe_layer_forward minus the workspace, plus
+ * err_word: a device int32 that receives this call's MOE_ERR_* bits (read it with
+ *   moe_get_device_error), or NULL to discard them.
+ * Returns MOE_EUNSUPPORTED, before any launch, when the call needs more scratch than the
+ * array holds (moe_layer_workspace_bytes() > MOE_NOALLOC_SCRATCH_BYTES; at E = 288,
+ * H = 4096, I = 2048 and S = R, that is beyond 2,800 rows).  Nothing in the array has to start at any
+ * value (every byte a call reads was written earlier in the same call), so nothing is
+ * cleared.  Calls on one GPU share its array: calls that can overlap on one GPU (other
+ * streams, other threads) race and must be serialized by the caller.
+ * ---------------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, int S,
+                              const int32_t* a_expert, const int32_t* a_src,
+                              const int32_t* a_dst, const float* a_w, int R, int T,
+                              uint16_t* out, int32_t* err_word, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------------
  * moe_layer_forward_w4a16 — the routed-expert layer in W4A16 arithmetic: the steps of

@@ -62,6 +62,8 @@ _SIGNATURES = {
                                _P, _P, ctypes.c_size_t, _P]),
     "moe_layer_forward_w4a16": (_I, [ctypes.POINTER(MoeLayerDesc), _P, _I, _P, _P, _P, _P, _I,
                                      _I, _P, _P, ctypes.c_size_t, _P]),
+    "moe_layer_forward_noalloc": (_I, [ctypes.POINTER(MoeLayerDesc), _P, _I, _P, _P, _P, _P, _I,
+                                       _I, _P, _P, _P]),
     "moe_hbm_read_probe": (_I, [_P, ctypes.c_size_t, _I, ctypes.c_uint32, _P, _P]),
     "moe_hbm_read_probe_variants": (_I, []),
     "moe_get_device_error": (_I, [_P, _P]),
@@ -196,6 +198,16 @@ def moe_hbm_read_probe(src, nbytes, variant, key, sink, stream=None):
 
 def moe_hbm_read_probe_variants():
     return int(load().moe_hbm_read_probe_variants())
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_forward_noalloc(desc, x, S, a_expert, a_src, a_dst, a_w, R, T, out, err_word=None,
+                              stream=None):
+    _check("moe_layer_forward_noalloc", load().moe_layer_forward_noalloc(
+        ctypes.byref(desc), _ptr(x), S, _ptr(a_expert), _ptr(a_src), _ptr(a_dst), _ptr(a_w), R, T,
+        _ptr(out), _ptr(err_word), _stream(stream)))
 
 
 def moe_get_device_error(err_word, stream=None):

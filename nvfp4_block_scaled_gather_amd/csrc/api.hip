@@ -1,9 +1,12 @@
 // C ABI of the library (declared in include/moe_nvfp4.h): argument validation on the
 // host, then kernel launches on the caller's stream.  No allocation, no synchronization
-// (except moe_get_device_error), no state beyond per-device launch-limit caches.
+// (except moe_get_device_error); the only state is the per-device address of the fixed
+// scratch array of moe_layer_forward_noalloc.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "common.h"
 
@@ -44,6 +47,38 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
   } while (0)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+// Scratch of moe_layer_forward_noalloc: one array per GPU, held by the loaded code object
+// until the process ends.  In host code `scratch` only names the symbol; its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is ever used.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the first call there).
+int scratch_on_current_device(uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "layer (no allocation): hipGetDevice");
+  REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_EUNSUPPORTED,
+          "layer (no allocation): device %d beyond the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "layer (no allocation): hipGetSymbolAddress(scratch)");
+    REQUIRE(p && aligned(p, 256), MOE_EHIP, "layer (no allocation): scratch address %p unusable", p);
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 constexpr int kMaxGroupKeys = 16000;  // E + T, LDS histograms of the grouping kernel
 constexpr int kMaxRowK = 8192;        // row kernels keep a row in registers
@@ -384,6 +419,26 @@ int moe_layer_forward(const moe_layer_desc* L, const uint16_t* x, int S, const i
   const LayerWs w = carve(L, S, R, T, (uint8_t*)workspace);
   REQUIRE(workspace_bytes >= w.bytes, MOE_EWORKSPACE, "layer: workspace %zu bytes < %zu needed",
           workspace_bytes, w.bytes);
+  return run_layer(L, x, S, a_expert, a_src, a_dst, a_w, R, T, out, w, stream);
+}
+
+int moe_layer_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, int S,
+                              const int32_t* a_expert, const int32_t* a_src,
+                              const int32_t* a_dst, const float* a_w, int R, int T,
+                              uint16_t* out, int32_t* err_word, hipStream_t stream) {
+  int st = check_layer_call(L, x, S, a_expert, a_src, a_dst, a_w, R, T, out);
+  if (st != MOE_OK) return st;
+  REQUIRE(aligned(err_word, 4), MOE_EINVAL, "layer: err_word not 4-byte aligned");
+  const size_t need = carve(L, S, R, T, nullptr).bytes;
+  REQUIRE(need <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_EUNSUPPORTED,
+          "layer (no allocation): this call needs %zu bytes of scratch, more than the library's "
+          "fixed %zu-byte array (use moe_layer_forward with a workspace)",
+          need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  uint8_t* base = nullptr;
+  st = scratch_on_current_device(&base);
+  if (st != MOE_OK) return st;
+  LayerWs w = carve(L, S, R, T, base);
+  if (err_word) w.err = err_word;
   return run_layer(L, x, S, a_expert, a_src, a_dst, a_w, R, T, out, w, stream);
 }
 

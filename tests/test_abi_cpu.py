@@ -154,6 +154,24 @@ def test_read_probe_rejects_bad_arguments_before_launch(lib):
     assert lib.moe_hbm_read_probe(ctypes.c_void_p(4104), unit, 0, 0, p16, None) == B.MOE_EINVAL
 
 
+def test_noalloc_layer_rejects_oversized_calls_before_any_device_call(lib):
+    """moe_layer_forward_noalloc refuses a call whose workspace exceeds its fixed scratch
+    array (and bad arguments) on the host, before it looks up the array on a device."""
+    p16 = ctypes.c_void_p(4096)
+    d = B.MoeLayerDesc(288, 4096, 2048, 4096, 4096, 4096, 4096, 4096, 0, 0)
+    big = 2900
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(d), big, big, 288) > B.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(d), p16, big, p16, p16, p16, p16, big, 288,
+                                         p16, None, None) == B.MOE_EUNSUPPORTED
+    assert b"scratch" in lib.moe_last_error()
+    assert lib.moe_layer_forward_noalloc(None, p16, 4, p16, p16, p16, p16, 8, 4, p16, None,
+                                         None) == B.MOE_EINVAL
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(d), p16, 4, p16, p16, p16, p16, 8, 4, p16,
+                                         ctypes.c_void_p(4098), None) == B.MOE_EINVAL
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_SCRATCH_BYTES
+
+
 def test_workspace_grows_with_rows(lib):
     d = B.MoeLayerDesc(288, 4096, 2048, 4096, 4096, 4096, 4096, 4096, 0, 4)
     a = lib.moe_layer_workspace_bytes(ctypes.byref(d), 570, 570, 8)

@@ -100,7 +100,7 @@ def calibrate_copy():
                       "bytes_written_per_copy": n, "copies": 3}), flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grouped_gemm_w13_ragged570_hbm_bytes.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_layer_ragged570_hbm_bytes.txt")
 
 
 def measured_traffic(workload):

@@ -63,6 +63,9 @@ constexpr int kMultiPassWCpol = 1;
 namespace moe {
 
 constexpr int kGemmWaves = 4;
+// s_waitcnt operand that waits for LDS (lgkmcnt 0) and leaves vector-memory loads and
+// exports in flight (vmcnt 63, expcnt 7: the largest counts, i.e. no wait).
+constexpr int kWaitLgkm0 = 0xC07F;
 constexpr int kPassRows = 16;  // activation rows per MFMA pass (the B operand's columns)
 constexpr int kGemvRows = 4;   // activation rows per GEMV pass
 
@@ -281,58 +284,105 @@ __device__ __forceinline__ uint32_t chunk_scales(const u32x4& g, int j) {
 // tile s and sg[s] the group's scales.  Loads in the main loop are unconditional and
 // pinned right after the use of their slot, so every wait is a counted one and the
 // prefetch distance stays D chunks.
-template <int NS, int D, int S, class Consume, int WC = MOE_W_CPOL>
-__device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC, int sstride,
-                                               int vw, int vs, Consume consume) {
+// The ring's registers: D chunks of NS tiles in flight, and the current scale group.
+template <int NS, int D>
+struct Ring {
   u32x4 wn[D][NS];
-  u32x4 cur[NS], nxt[NS];
-  auto load_nib = [&](int c, int slot) {
-    const int g = c / S, j = c - g * S;
+  u32x4 cur[NS];
+};
+
+template <int NS, int S, int WC>
+__device__ __forceinline__ void ring_load_nib(u32x4 (&dst)[NS], __amdgpu_buffer_rsrc_t wr,
+                                              int sstride, int vw, int c) {
+  const int g = c / S, j = c - g * S;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      wn[slot][s] = __builtin_amdgcn_raw_buffer_load_b128(
-          wr, vw, s * sstride + g * S * kChunkBytes + j * 1024, WC);
-  };
-  auto load_scales = [&](int g, u32x4 (&sg)[NS]) {
+  for (int s = 0; s < NS; ++s)
+    dst[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, vw, s * sstride + g * S * kChunkBytes +
+                                                               j * 1024, WC);
+}
+
+template <int NS, int S, int WC>
+__device__ __forceinline__ void ring_load_scales(u32x4 (&dst)[NS], __amdgpu_buffer_rsrc_t wr,
+                                                 int sstride, int vs, int g) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      sg[s] = load_scale_group<S, WC>(wr, vs, s * sstride + g * S * kChunkBytes);
-  };
-  const int NG = NC / S;
-  load_scales(0, cur);
+  for (int s = 0; s < NS; ++s)
+    dst[s] = load_scale_group<S, WC>(wr, vs, s * sstride + g * S * kChunkBytes);
+}
+
+// The ring's first loads: scale group 0 (unless P0 > 0) and chunks P0 .. P-1.
+template <int NS, int D, int S, int WC, int P = D, int P0 = 0>
+__device__ __forceinline__ void ring_prime(Ring<NS, D>& rg, __amdgpu_buffer_rsrc_t wr,
+                                           int sstride, int vw, int vs) {
+  static_assert(0 <= P0 && P0 <= P && P <= D, "chunks P0 .. P-1 of the ring");
+  if constexpr (P0 == 0) ring_load_scales<NS, S, WC>(rg.cur, wr, sstride, vs, 0);
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load_nib(d, d);
+  for (int d = P0; d < P; ++d) {
+    ring_load_nib<NS, S, WC>(rg.wn[d], wr, sstride, vw, d);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Streams NS tiles (buffer wr, tiles sstride bytes apart) over all of K in scale groups of
+// S chunks with a ring of D chunks (D <= S, both powers of two, S divides NC = K / 128).
+// consume(c, j, wn, sg) uses chunk c (chunk j of its group): wn[s] holds its nibbles for
+// tile s and sg[s] the group's scales.  Loads in the main loop are unconditional and
+// pinned right after the use of their slot, so every wait is a counted one and the
+// prefetch distance stays D chunks.  PRIMED > 0: the caller has issued the scale group and
+// the first PRIMED chunks of the ring (ring_prime<..., PRIMED>) into rg already, earlier,
+// so that their latency overlaps its own work; the rest are issued here.
+template <int NS, int D, int S, class Consume, int WC = MOE_W_CPOL, int PRIMED = 0>
+__device__ __forceinline__ void stream_weights(__amdgpu_buffer_rsrc_t wr, int NC, int sstride,
+                                               int vw, int vs, Consume consume,
+                                               Ring<NS, D>& rg) {
+  u32x4 nxt[NS];
+  const int NG = NC / S;
+  if constexpr (PRIMED == 0) ring_prime<NS, D, S, WC>(rg, wr, sstride, vw, vs);
+  else ring_prime<NS, D, S, WC, D, PRIMED>(rg, wr, sstride, vw, vs);
   int g = 0;
   for (; g + 1 < NG; ++g) {
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-      consume(g * S + j, j, wn[j % D], cur);
+      consume(g * S + j, j, rg.wn[j % D], rg.cur);
       __builtin_amdgcn_sched_barrier(0);
-      if (j == S - D) load_scales(g + 1, nxt);  // with the first refill of the next group
-      load_nib(g * S + j + D, j % D);
+      if (j == S - D) ring_load_scales<NS, S, WC>(nxt, wr, sstride, vs, g + 1);  // with the
+                                                                              // first refill
+      ring_load_nib<NS, S, WC>(rg.wn[j % D], wr, sstride, vw, g * S + j + D);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int s = 0; s < NS; ++s) cur[s] = nxt[s];
+    for (int s = 0; s < NS; ++s) rg.cur[s] = nxt[s];
   }
 #pragma unroll
   for (int j = 0; j < S; ++j) {  // last group: refill only inside it
-    consume(g * S + j, j, wn[j % D], cur);
+    consume(g * S + j, j, rg.wn[j % D], rg.cur);
     if (j + D < S) {
       __builtin_amdgcn_sched_barrier(0);
-      load_nib(g * S + j + D, j % D);
+      ring_load_nib<NS, S, WC>(rg.wn[j % D], wr, sstride, vw, g * S + j + D);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-template <int NS, int D, int S, int WC, class Consume>
+template <int NS, int D, int S, int WC, int PRIMED = 0, class Consume>
 __device__ __forceinline__ void stream_weights_c(__amdgpu_buffer_rsrc_t wr, int NC, int sstride,
-                                                 int vw, int vs, Consume consume) {
-  stream_weights<NS, D, S, Consume, WC>(wr, NC, sstride, vw, vs, consume);
+                                                 int vw, int vs, Consume consume,
+                                                 Ring<NS, D>& rg) {
+  stream_weights<NS, D, S, Consume, WC, PRIMED>(wr, NC, sstride, vw, vs, consume, rg);
+}
+
+// The weight buffer of a pass's NS tiles (wt: the first, uniform; nsv: tiles this wave
+// has, <= 0 for none: an empty range, so its loads return zeros and touch nothing) and the
+// distance between its tiles (SWI: a gate tile and the up tile I/16 tiles after it).
+template <bool SWI>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pass_weights(const GemmArgs& p,
+                                                               const uint8_t* wt, int nsv,
+                                                               int& sstride) {
+  const int tstride = (p.K / 128) * kChunkBytes;
+  sstride = SWI ? (p.I / 16) * tstride : tstride;
+  const int range = nsv <= 0 ? 0 : SWI ? sstride + tstride : nsv * tstride;
+  // (readfirstlane: the clamp may be computed on the vector unit, and a descriptor the
+  // compiler believes divergent turns every load into a loop over lanes)
+  return make_rsrc(wt, __builtin_amdgcn_readfirstlane(range));
 }
 
 // ------------------------------------------------------------------------- MFMA path
@@ -347,26 +397,30 @@ __device__ __forceinline__ void stream_weights_c(__amdgpu_buffer_rsrc_t wr, int 
 // expert's down global of the scatter-ready epilogue.
 //
 // FQ: the pass's rows are already quantized into the staging area and their row globals
-// are in s_rgs (the decode-sized w13 GEMM below); nothing is staged from global memory.
+// are in s_rgs (the decode-sized GEMMs below); nothing is staged from global memory.
+// PRIMED > 0 (with FQ): the caller issued the scale group and the first PRIMED chunks of
+// this pass's weight ring into *ext before it quantized the rows (ring_prime<..., PRIMED>
+// on pass_weights<SWI>(p, wt, nsv, .)), so that their latency overlapped the quantization.
+// With FQ the barrier below waits for LDS only, leaving weight loads in flight.
 template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, bool FQ = false,
-          int WPOL = MOE_W_CPOL>
+          int WPOL = MOE_W_CPOL, int PRIMED = 0>
 __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0,
                                           uint8_t* s_q, uint8_t* s_s, float ggate, float gup,
-                                          const float* s_rgs = nullptr) {
+                                          const float* s_rgs = nullptr,
+                                          Ring<NS, D>* ext = nullptr) {
   static_assert(!SWI || NS == 2, "the SwiGLU epilogue pairs one gate and one up tile");
+  static_assert(PRIMED == 0 || FQ, "only rows quantized in place overlap the first loads");
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4, r = lane & 15;
   const int K = p.K, NC = K / 128;
   // Passes of one item load the same weight chunks; keep the compiler from hoisting those
   // loads out of the pass loop (it would hold a second copy of the ring in registers).
-  asm volatile("" ::: "memory");
-  const int tstride = NC * kChunkBytes;
-  const int sstride = SWI ? (p.I / 16) * tstride : tstride;
-  const int range = nsv <= 0 ? 0 : SWI ? sstride + tstride : nsv * tstride;
-  // (readfirstlane: the clamp may be computed on the vector unit, and a descriptor the
-  // compiler believes divergent turns every load into a loop over lanes)
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(wt, __builtin_amdgcn_readfirstlane(range));
+  if constexpr (PRIMED == 0) asm volatile("" ::: "memory");
+  int sstride;
+  const __amdgpu_buffer_rsrc_t wr = pass_weights<SWI>(p, wt, nsv, sstride);
+  Ring<NS, D> own;
+  Ring<NS, D>& rg = PRIMED > 0 ? *ext : own;
   // scatter-ready epilogue: this lane's coefficient inputs, loaded now so the epilogue
   // does not wait on them
   float ow = 0.f, ogs = 1.f;
@@ -375,9 +429,19 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     if (!FQ && p.c_gs) ogs = p.c_gs[arow0 + r];
   }
 
-  if (!FQ) stage_rows<ABF, WAVES>(p, arow0, nrows, s_q, s_s);
-  __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
-  __syncthreads();
+  if constexpr (FQ) {
+    // the rows were written to LDS by this workgroup's threads: wait for those writes
+    // only (the primed weight loads stay in flight), then meet at the barrier; the
+    // compiler barriers keep LDS accesses on their side of it
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  } else {
+    stage_rows<ABF, WAVES>(p, arow0, nrows, s_q, s_s);
+    __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
+    __syncthreads();
+  }
 
   const int rl = r < nrows ? r : 0;
   f32x4 acc[NS];
@@ -392,7 +456,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     u32x4 b_next[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) b_next[q] = *(const u32x4*)(ab_l + 16 * q);
-    stream_weights_c<NS, D, S, WPOL>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
+    stream_weights_c<NS, D, S, WPOL, PRIMED>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
                              [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
       u32x4 bq[4];
 #pragma unroll
@@ -412,7 +476,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
                                                            acc[s], 0, 0, 0);
         }
       }
-    });
+    }, rg);
   } else {
     const uint8_t* aq_l = s_q + rl * q_stride(K) + 16 * kq;
     const uint8_t* as_l = s_s + rl * s_stride(K) + 2 * kq;
@@ -420,7 +484,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     // chunk past the end land in the row padding, the next region or the slack: never used).
     u32x4 an_next = *(const u32x4*)aq_l;
     uint32_t asc_next = *(const uint16_t*)as_l;
-    stream_weights_c<NS, D, S, WPOL>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
+    stream_weights_c<NS, D, S, WPOL, PRIMED>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
                              [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
       const u32x4 an = an_next;
       const uint32_t asc = asc_next;
@@ -440,7 +504,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
           acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[q], acc[s], 0, 0, 0);
         }
       }
-    });
+    }, rg);
   }
 
   // Lane l holds out row r x weight rows 4 kq .. 4 kq + 3 of each tile.  The workgroup's
@@ -558,41 +622,56 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
 // what).
 constexpr int kSmallGroupRows = 32;
 
-// Quantize nrows bf16 rows of K columns (row_ptr(r): row r's first element, nullptr: an
+// Quantize nrows bf16 rows of K columns (K <= 4096 BPT, BPT 16-element blocks per thread;
+// RPS rows' loads in flight at a time; row_ptr(r): row r's first element, nullptr: an
 // all-zero row) into the staging area, row r at s_q + r q_stride(K) / s_s + r s_stride(K)
 // and its row global at s_rgs[r], with the quantizer of the row kernels (every thread of
-// the workgroup takes part; two rows' loads in flight at a time).  The caller synchronizes
-// before the staged rows are read.
-template <class RowPtr>
+// the workgroup takes part).  after_first_loads() runs
+// once, after the first rows' loads are issued and before they are waited for (the caller
+// issues its first weight loads there, so that their latency overlaps the quantization;
+// loads complete in order, so they must come after the rows' loads).  The caller
+// synchronizes before the staged rows are read.
+template <int BPT, int RPS, class RowPtr, class AfterLoads>
 __device__ __forceinline__ void quantize_rows_to_lds(RowPtr row_ptr, int nrows, int K,
                                                      uint8_t* s_q, uint8_t* s_s, float* s_rgs,
-                                                     float* s_red) {
+                                                     float* s_red, AfterLoads after_first_loads) {
   constexpr int NT = 64 * kGemmWaves;  // threads per row: block b = t + NT k of each row
   const int NB = K / 16, t = threadIdx.x;
-  for (int r = 0; r < nrows; r += 2) {
-    float v[2][2][16];
+  for (int r = 0; r < nrows; r += RPS) {
+    u32x4 w[RPS][BPT][2];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < RPS; ++rr) {
       const uint16_t* src = r + rr < nrows ? row_ptr(r + rr) : nullptr;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < BPT; ++k) {
         const int blk = t + NT * k;
-        u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+        w[rr][k][0] = w[rr][k][1] = u32x4{0u, 0u, 0u, 0u};
         if (src && blk < NB) {
           const u32x4* px = (const u32x4*)(src + 16 * blk);
-          w0 = px[0];
-          w1 = px[1];
+          w[rr][k][0] = px[0];
+          w[rr][k][1] = px[1];
         }
-        bf16x16_to_f32(w0, w1, v[rr][k]);
       }
     }
+    if (r == 0) {  // uniform: after the first rows' loads, before they are waited for
+      __builtin_amdgcn_sched_barrier(0);
+      after_first_loads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float v[RPS][BPT][16];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < RPS; ++rr)
+#pragma unroll
+      for (int k = 0; k < BPT; ++k) bf16x16_to_f32(w[rr][k][0], w[rr][k][1], v[rr][k]);
+#pragma unroll
+    for (int rr = 0; rr < RPS; ++rr) {
       // every thread joins the row-max barrier; only real rows store
-      const float amax = row_amax_threads<2>(v[rr], t, NT, s_red + rr * kGemmWaves);
+      // (consecutive rows alternate between two slots of s_red: a slot is rewritten only
+      // after the barrier of the next row, which every wave reaches after its reads)
+      const float amax = row_amax_threads<BPT>(v[rr], t, NT, s_red + ((r + rr) & 1) * kGemmWaves);
       if (r + rr < nrows)
-        quantize_row_store<2>(v[rr], NB, t, NT, amax, s_q + (r + rr) * q_stride(K),
-                              s_s + (r + rr) * s_stride(K), s_rgs + r + rr);
+        quantize_row_store<BPT>(v[rr], NB, t, NT, amax, s_q + (r + rr) * q_stride(K),
+                                s_s + (r + rr) * s_stride(K), s_rgs + r + rr);
     }
   }
 }
@@ -615,7 +694,7 @@ struct GroupArgs {
 
 // ABF (W4A16): the source rows are bf16 activations used as they are (copied into the
 // staging area, row global 1), in passes of 4 rows like the small-batch W4A16 instance.
-template <int D, int S, bool ABF>
+template <int D, int S, bool ABF, int BPT>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmArgs p, GroupArgs q) {
   constexpr int PR = ABF ? 4 : kPassRows;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -683,6 +762,10 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
   const size_t tile_bytes = (size_t)9 * p.K;
   const uint8_t* wt = p.w + (size_t)eg * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
   const float ggate = p.g_gate[eg], gup = p.g_up[eg];
+  // NVFP4: the first pass's weight loads go out while its rows are being quantized
+  Ring<2, D> rg;
+  int sstride;
+  const __amdgpu_buffer_rsrc_t wr = pass_weights<true>(p, wt, nsv, sstride);
   for (int b = 0; b < G; b += PR) {
     if (b) __syncthreads();  // the previous pass is done with the staged rows
     const int nrows = min(PR, G - b);
@@ -694,12 +777,24 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
         *(u32x4*)(s_q + r * b_stride(p.K) + 16 * c) = v;
       }
       if (threadIdx.x < nrows) s_rgs[threadIdx.x] = 1.0f;
+      mfma_pass<2, D, S, true, ABF, kGemmWaves, true>(p, wt, nsv, r0 + b, nrows, 16 * t0, s_q,
+                                                      s_s, ggate, gup, s_rgs);
     } else {
-      quantize_rows_to_lds([&](int r) { return q.x + (size_t)s_src[b + r] * p.K; }, nrows, p.K,
-                           s_q, s_s, s_rgs, s_red);
+      auto rows = [&](int r) { return q.x + (size_t)s_src[b + r] * p.K; };
+      if (b == 0) {  // one row at a time here: the ring's registers are live
+        // (half the ring: the other half's registers would cost occupancy at 4 tokens)
+        constexpr int P = D / 2 > 0 ? D / 2 : 1;
+        quantize_rows_to_lds<BPT, 1>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, [&] {
+          ring_prime<2, D, S, MOE_W_CPOL, P>(rg, wr, sstride, 16 * lane, S * 1024 + 2 * S * lane);
+        });
+        mfma_pass<2, D, S, true, false, kGemmWaves, true, MOE_W_CPOL, P>(
+            p, wt, nsv, r0 + b, nrows, 16 * t0, s_q, s_s, ggate, gup, s_rgs, &rg);
+      } else {
+        quantize_rows_to_lds<BPT, 2>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, [] {});
+        mfma_pass<2, D, S, true, false, kGemmWaves, true>(p, wt, nsv, r0 + b, nrows, 16 * t0,
+                                                          s_q, s_s, ggate, gup, s_rgs);
+      }
     }
-    mfma_pass<2, D, S, true, ABF, kGemmWaves, true>(p, wt, nsv, r0 + b, nrows, 16 * t0, s_q,
-                                                    s_s, ggate, gup, s_rgs);
   }
 }
 
@@ -709,7 +804,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
 // quantization launch between the two GEMMs; the scatter coefficient takes the row global
 // it has just computed.  Items, passes and arithmetic are those of k_gemm_mfma's
 // small-batch instance: the same bits.
-template <int D, int S>
+template <int D, int S, int BPT>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_quantizing(GemmArgs p,
                                                                      const uint16_t* __restrict__ h) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -729,14 +824,27 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_quantizing(GemmArgs p,
   const size_t tile_bytes = (size_t)9 * p.K;
   const uint8_t* wt = p.w + (size_t)g.e * expert_bytes + (size_t)(nsv > 0 ? t0 : 0) * tile_bytes;
   const float gdown = p.c_g[g.e];
+  // the first pass's weight loads go out while its rows of h are being quantized
+  const int lane = threadIdx.x & 63;
+  Ring<1, D> rg;
+  int sstride;
+  const __amdgpu_buffer_rsrc_t wr = pass_weights<false>(p, wt, nsv, sstride);
   for (int b = 0; b < g.G; b += kPassRows) {
     if (b) __syncthreads();  // the previous pass is done with the staged rows
     const int nrows = min(kPassRows, g.G - b);
     const int row0 = g.r0 + b;
-    quantize_rows_to_lds([&](int r) { return h + (size_t)(row0 + r) * p.K; }, nrows, p.K, s_q,
-                         s_s, s_rgs, s_red);
-    mfma_pass<1, D, S, false, false, kGemmWaves, true>(p, wt, nsv, row0, nrows, 16 * t0, s_q,
-                                                       s_s, gdown, 0.f, s_rgs);
+    auto rows = [&](int r) { return h + (size_t)(row0 + r) * p.K; };
+    if (b == 0) {  // one row at a time here: the ring's registers are live
+      quantize_rows_to_lds<BPT, 1>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, [&] {
+        ring_prime<1, D, S, MOE_W_CPOL>(rg, wr, sstride, 16 * lane, S * 1024 + 2 * S * lane);
+      });
+      mfma_pass<1, D, S, false, false, kGemmWaves, true, MOE_W_CPOL, D>(
+          p, wt, nsv, row0, nrows, 16 * t0, s_q, s_s, gdown, 0.f, s_rgs, &rg);
+    } else {
+      quantize_rows_to_lds<BPT, 2>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, [] {});
+      mfma_pass<1, D, S, false, false, kGemmWaves, true>(p, wt, nsv, row0, nrows, 16 * t0, s_q,
+                                                         s_s, gdown, 0.f, s_rgs);
+    }
   }
 }
 
@@ -766,6 +874,7 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
 #pragma unroll
     for (int a = 0; a < NR; ++a) acc[s][a] = 0.f;
 
+  Ring<NS, D> rg;
   stream_weights<NS, D, S>(wr, NC, tstride, 16 * lane, S * 1024 + 2 * S * lane,
                            [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
 #pragma unroll
@@ -796,7 +905,7 @@ __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __re
         acc[s][a] = fmaf(sw1, b1, acc[s][a]);
       }
     }
-  });
+  }, rg);
 
 #pragma unroll
   for (int a = 0; a < NR; ++a) {
@@ -1030,11 +1139,20 @@ static hipError_t launch_swiglu_grouping_t(const int32_t* a_expert, const int32_
     hipLaunchKernelGGL(kern, grid, block, lds, s, a, g);
     return hipGetLastError();
   };
+  // (a thread quantizes one 16-element block of each row up to K = 4096, two above)
+  if (K <= 64 * kGemmWaves * 16) {
+    switch (scale_group(K / 128)) {
+      case 8: return go(k_gemm_swiglu_grouping<8, 8, ABF, 1>);
+      case 4: return go(k_gemm_swiglu_grouping<4, 4, ABF, 1>);
+      case 2: return go(k_gemm_swiglu_grouping<2, 2, ABF, 1>);
+      default: return go(k_gemm_swiglu_grouping<1, 1, ABF, 1>);
+    }
+  }
   switch (scale_group(K / 128)) {
-    case 8: return go(k_gemm_swiglu_grouping<8, 8, ABF>);
-    case 4: return go(k_gemm_swiglu_grouping<4, 4, ABF>);
-    case 2: return go(k_gemm_swiglu_grouping<2, 2, ABF>);
-    default: return go(k_gemm_swiglu_grouping<1, 1, ABF>);
+    case 8: return go(k_gemm_swiglu_grouping<8, 8, ABF, 2>);
+    case 4: return go(k_gemm_swiglu_grouping<4, 4, ABF, 2>);
+    case 2: return go(k_gemm_swiglu_grouping<2, 2, ABF, 2>);
+    default: return go(k_gemm_swiglu_grouping<1, 1, ABF, 2>);
   }
 }
 
@@ -1071,11 +1189,19 @@ hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expe
     hipLaunchKernelGGL(kern, grid, block, lds, s, a, h);
     return hipGetLastError();
   };
+  if (K <= 64 * kGemmWaves * 16) {
+    switch (scale_group(K / 128)) {
+      case 8: return go(k_gemm_quantizing<8, 8, 1>);
+      case 4: return go(k_gemm_quantizing<4, 4, 1>);
+      case 2: return go(k_gemm_quantizing<2, 2, 1>);
+      default: return go(k_gemm_quantizing<1, 1, 1>);
+    }
+  }
   switch (scale_group(K / 128)) {
-    case 8: return go(k_gemm_quantizing<8, 8>);
-    case 4: return go(k_gemm_quantizing<4, 4>);
-    case 2: return go(k_gemm_quantizing<2, 2>);
-    default: return go(k_gemm_quantizing<1, 1>);
+    case 8: return go(k_gemm_quantizing<8, 8, 2>);
+    case 4: return go(k_gemm_quantizing<4, 4, 2>);
+    case 2: return go(k_gemm_quantizing<2, 2, 2>);
+    default: return go(k_gemm_quantizing<1, 1, 2>);
   }
 }
 

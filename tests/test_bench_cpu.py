@@ -30,8 +30,10 @@ def test_traffic_summary_matches_the_algorithmic_bytes_and_the_sources():
     assert int(fields["algorithmic_bytes_per_launch"]) == alg
     traffic = int(fields["traffic_bytes_per_launch"])
     assert alg <= traffic < 1.05 * alg          # every weight byte read from HBM once
-    assert fields["kernel_sources_sha256"] == build.kernel_source_hash()
-    assert bench.measured_traffic("ragged570") == traffic
+    # the figure is reported only while the summary was taken at the current GEMM sources;
+    # after a change to them it is withheld (null) until the counters are taken again
+    fresh = fields["kernel_sources_sha256"] == build.kernel_source_hash()
+    assert bench.measured_traffic("ragged570") == (traffic if fresh else None)
     assert bench.measured_traffic("ragged2303") is None  # summary is for ragged570 only
 
 

@@ -261,6 +261,7 @@ struct LayerWs {
   uint8_t* hs;
   float* hgs;
   uint16_t* h16;  // W4A16: h [R, I] bf16 (the w2 GEMM's input while acc takes its output)
+  int4* items;    // the grouped GEMMs' work list, E + 1 entries
   size_t bytes;
 };
 
@@ -290,6 +291,7 @@ LayerWs carve(const moe_layer_desc* L, int S, int R, int T, uint8_t* base) {
   w.hs = take(r * L->I / 16);
   w.hgs = (float*)take(4 * r);
   w.h16 = (uint16_t*)take(2 * r * L->I);
+  w.items = (int4*)take(sizeof(int4) * ((size_t)L->E + 1));
   w.bytes = o;
   return w;
 }
@@ -368,9 +370,11 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
   }
   // grouping + NVFP4 quantization of the S source rows (one launch); the w13 GEMM reads
   // grouped row i from source row row_src[i], so no gathered copy of x is made
+  // (the work list is written and used only when every group is on the MFMA path)
+  int4* items = all_mfma && R > 32 ? w.items : nullptr;
   e = moe::launch_group_quantize(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
                                  w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, x, H, w.xq,
-                                 w.xs, w.xgs, stream);
+                                 w.xs, w.xgs, items, stream);
   if (e != hipSuccess) return hip_status(e, "layer: group+quantize launch");
   if (all_mfma) {
     // SwiGLU in the w13 GEMM's epilogue (h in bf16 instead of the fp32 gate|up products),
@@ -379,7 +383,7 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
     if (R > 0) {
       e = moe::launch_grouped_gemm_swiglu(w.xq, w.xs, w.row_src, S, w.offsets, E, R,
                                           (const uint8_t*)L->w13_packed, I, H, L->g_gate, L->g_up,
-                                          w.xgs, w.row_src, h, stream);
+                                          w.xgs, w.row_src, h, stream, items);
       if (e != hipSuccess) return hip_status(e, "layer: w13 GEMM + SwiGLU launch");
     }
     e = moe::launch_quantize(h, nullptr, w.offsets + E, R, I, w.hq, w.hs, w.hgs, stream);
@@ -400,7 +404,7 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
   if (R > 0) {
     e = moe::launch_grouped_gemm(w.hq, w.hs, nullptr, R, w.offsets, E, R,
                                  (const uint8_t*)L->w2_packed, H, I, w.acc, L->flags,
-                                 L->gemv_max_rows, stream, w.row_w, L->g_down, w.hgs);
+                                 L->gemv_max_rows, stream, w.row_w, L->g_down, w.hgs, items);
     if (e != hipSuccess) return hip_status(e, "layer: w2 GEMM launch");
   }
   e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);

@@ -350,6 +350,12 @@ __device__ __forceinline__ void group_small(const int32_t* __restrict__ a_expert
   if (lane == 0) *err_word = err;
 }
 
+// The grouped GEMM's work list, written by the grouping: the non-empty groups in the order
+// the GEMM's items take them, groups of more than this many rows (one pass of activation
+// rows) first.  items[0] = {groups, groups of more than kWorkListMultiRows rows},
+// items[1 + a] = {expert, first grouped row, rows} of group a.
+constexpr int kWorkListMultiRows = 16;
+
 // Threads per row for NB scale blocks: a multiple of 64, at most 256.
 static inline int row_threads(int NB) {
   const int t = ((NB + 63) / 64) * 64;
@@ -382,11 +388,13 @@ hipError_t launch_swiglu(const float* acc13, int R, int I, const int32_t* expert
 // With c_w: grouped row i of expert e is multiplied by the fp32 product
 // c_w[i] * c_g[e] * c_gs[i] (each term of the scatter-add).
 // R: the grouped rows (expert_offsets[E] <= R), which bounds the non-empty groups.
+// items: the grouping's work list (kWorkListMultiRows) for this batch, or nullptr.
 hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32_t* amap,
                                int a_rows, const int32_t* expert_offsets, int E, int R,
                                const uint8_t* w, int N, int K, float* out, int flags,
                                int gemv_max_rows, hipStream_t s, const float* c_w = nullptr,
-                               const float* c_g = nullptr, const float* c_gs = nullptr);
+                               const float* c_g = nullptr, const float* c_gs = nullptr,
+                               const int4* items = nullptr);
 // The w13 GEMM with SwiGLU applied in its epilogue (MFMA path for every group): the
 // fused [2I, K] gate|up weights give h [R, I] bf16 for the grouped rows, equal bit for bit
 // to launch_grouped_gemm followed by launch_swiglu.  Rows outside every group are not
@@ -395,7 +403,8 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, cons
                                       int a_rows, const int32_t* expert_offsets, int E, int R,
                                       const uint8_t* w13, int I, int K, const float* g_gate,
                                       const float* g_up, const float* row_gs,
-                                      const int32_t* gs_map, uint16_t* h, hipStream_t s);
+                                      const int32_t* gs_map, uint16_t* h, hipStream_t s,
+                                      const int4* items = nullptr);
 // The same for a batch of 1..32 assignments, with the grouping of launch_group and the
 // quantization of the source rows x [S, K] done inside the launch (the grouping outputs are
 // written as launch_group writes them; the quantized rows stay in LDS).  bf16_acts: the
@@ -428,13 +437,15 @@ hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* a
                                             const uint8_t* w13, int I, int K, const float* g_gate,
                                             const float* g_up, uint16_t* h, hipStream_t s);
 // Grouping and NVFP4 quantization of the S source rows of x in one launch (independent
-// work: block 0 groups, the other blocks quantize four rows each).
+// work: block 0 groups, the other blocks quantize four rows each).  items (E + 1 entries,
+// or nullptr): for more than 32 assignments, also the grouped GEMM's work list (see
+// kWorkListMultiRows).
 hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
                                  const float* a_w, int R, int E, int S, int T,
                                  int32_t* expert_offsets, int32_t* row_src, int32_t* row_dst,
                                  float* row_w, int32_t* tok_off, int32_t* tok_rows,
                                  int32_t* err_word, const uint16_t* x, int H, uint8_t* xq,
-                                 uint8_t* xs, float* xgs, hipStream_t s);
+                                 uint8_t* xs, float* xgs, int4* items, hipStream_t s);
 hipError_t launch_scatter(const float* y, int R, int H, const int32_t* expert_offsets, int E,
                           const float* row_w, const float* g_down, const float* row_gs,
                           const int32_t* tok_off, const int32_t* tok_rows, int T, uint16_t* out,

@@ -95,6 +95,9 @@ struct GemmArgs {
   const float* c_gs;       // nullptr: 1 (bf16 activations carry no row global)
   // W4A16: bf16 activation rows [a_rows, K] (through amap) in place of aq / as
   const uint16_t* ab;
+  // The grouping's work list (kWorkListMultiRows), or nullptr: workgroups then scan the
+  // offsets.  Only for launches that own every group (gmin <= 1, no upper bound).
+  const int4* items;
 };
 
 // ------------------------------------------------------------------------- LDS layout
@@ -133,6 +136,16 @@ struct ItemGroup {
 
 template <int PR>
 __device__ __forceinline__ bool find_group(const GemmArgs& p, int ai, int* s_grp, ItemGroup& g) {
+  if (PR == kWorkListMultiRows && p.items) {
+    // the grouping's work list has the groups in this order: one load (ai < min(E, R) <= E,
+    // so the entry is inside the list even when it is past the last group)
+    const int4 h = p.items[0];
+    const int4 it = p.items[1 + ai];
+    g.e = __builtin_amdgcn_readfirstlane(it.x);
+    g.r0 = __builtin_amdgcn_readfirstlane(it.y);
+    g.G = __builtin_amdgcn_readfirstlane(it.z);
+    return ai < __builtin_amdgcn_readfirstlane(h.x);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -1019,9 +1032,11 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, cons
                                       int a_rows, const int32_t* off, int E, int R,
                                       const uint8_t* w13, int I, int K, const float* g_gate,
                                       const float* g_up, const float* row_gs,
-                                      const int32_t* gs_map, uint16_t* h, hipStream_t s) {
+                                      const int32_t* gs_map, uint16_t* h, hipStream_t s,
+                                      const int4* items) {
   GemmArgs a{aq, as, amap, a_rows, off, E, w13, 2 * I, K, nullptr, 1, 0x7FFFFFFF,
              g_gate, g_up, row_gs, gs_map, h, I};
+  a.items = items;
   // one gate tile per wave: (I/16)/4 items per expert, the grid of N = 2I with 8 per item
   if (small_grid(a, R)) return launch_mfma_t<2, 8, true>(a, 2 * kGemmWaves, R, s);
   return launch_mfma_t<2, MOE_GEMM_D, true>(a, 2 * kGemmWaves, R, s);
@@ -1031,7 +1046,7 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
                                int a_rows, const int32_t* off, int E, int R, const uint8_t* w,
                                int N, int K, float* out, int flags, int gemv_max_rows,
                                hipStream_t s, const float* c_w, const float* c_g,
-                               const float* c_gs) {
+                               const float* c_gs, const int4* items) {
   const int big = 0x7FFFFFFF;
   // which groups each kernel owns
   int gemv_lo = 1, gemv_hi = 0, mfma_lo = 1;
@@ -1055,6 +1070,7 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
     a.c_w = c_w;
     a.c_g = c_g;
     a.c_gs = c_gs;
+    if (mfma_lo <= 1) a.items = items;  // the work list covers every group
     const hipError_t err = launch_mfma(a, R, s);
     if (err != hipSuccess) return err;
   }

@@ -154,7 +154,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
                            int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
                            float* __restrict__ row_w, int32_t* __restrict__ tok_off,
                            int32_t* __restrict__ tok_rows, int32_t* __restrict__ err_word,
-                           bool parallel, int* lds) {
+                           bool parallel, int* lds, int4* __restrict__ items = nullptr) {
   int* cnt_e = lds;                     // E + 1 (bucket E = dropped assignments)
   int* cnt_t = lds + (E + 1);           // T + 1
   int* hist = lds + (E + 1) + (T + 1);  // kGroupWaves x (max(E, T) + 1) when parallel
@@ -231,6 +231,27 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
   }
   if (tid == 0) *err_word = s_err;
   const int Rv = cnt_e[E];
+  // 2b. the GEMMs' work list (when asked for): the non-empty groups in the order the grouped
+  // GEMM takes them, groups of more than kWorkListMultiRows rows first, each set in ascending
+  // expert id; items[0] = {groups, groups of the first set}, items[1 + a] = {expert, first
+  // row, rows} of group a.  With it a GEMM workgroup finds its group with one load instead of
+  // a scan of the offsets.  Wave 0 alone, from the offsets in LDS.
+  if (items && tid < 64) {
+    const uint64_t below = tid ? (~0ull >> (64 - tid)) : 0ull;
+    int n = 0, n_multi = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int base = 0; base < E; base += 64) {  // uniform
+        const int e = base + tid;
+        const int G = e < E ? cnt_e[e + 1] - cnt_e[e] : 0;
+        const bool sel = pass == 0 ? G > kWorkListMultiRows : (G > 0 && G <= kWorkListMultiRows);
+        const uint64_t m = __ballot(sel);
+        if (sel) items[1 + n + __popcll(m & below)] = int4{e, cnt_e[e], G, 0};
+        n += __popcll(m);
+      }
+      if (pass == 0) n_multi = n;
+    }
+    if (tid == 0) items[0] = int4{n, n_multi, 0, 0};
+  }
   __syncthreads();
   // 3. grouped rows in (expert, assignment) order; dropped assignments last
   if constexpr (CACHED) {
@@ -300,19 +321,19 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_quantize(
     float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
     int32_t* __restrict__ err_word, bool parallel, bool cached,
     const uint16_t* __restrict__ x, int H, int nthreads, uint8_t* __restrict__ xq,
-    uint8_t* __restrict__ xs, float* __restrict__ xgs) {
+    uint8_t* __restrict__ xs, float* __restrict__ xgs, int4* __restrict__ items) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   __shared__ float s_red[kGroupWaves];
   if (blockIdx.x == 0) {
-    if (R <= kSmallGroupRows)
+    if (R <= kSmallGroupRows)  // (no work list: the GEMMs scan the offsets)
       group_small(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
                   row_w, tok_off, tok_rows, err_word);
     else if (cached)
       group_body<true>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
-                       row_w, tok_off, tok_rows, err_word, parallel, lds);
+                       row_w, tok_off, tok_rows, err_word, parallel, lds, items);
     else
       group_body<false>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
-                        row_w, tok_off, tok_rows, err_word, parallel, lds);
+                        row_w, tok_off, tok_rows, err_word, parallel, lds, items);
     return;
   }
   const int rows_per_block = kGroupThreads / nthreads;
@@ -377,7 +398,7 @@ hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, 
                                  int32_t* expert_offsets, int32_t* row_src, int32_t* row_dst,
                                  float* row_w, int32_t* tok_off, int32_t* tok_rows,
                                  int32_t* err_word, const uint16_t* x, int H, uint8_t* xq,
-                                 uint8_t* xs, float* xgs, hipStream_t s) {
+                                 uint8_t* xs, float* xgs, int4* items, hipStream_t s) {
   const bool par = group_parallel(E, T), cached = group_cached(E, T, R);
   const int NB = H / 16, nt = row_threads(NB);
   const int rows_per_block = kGroupThreads / nt;
@@ -388,13 +409,13 @@ hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_group_quantize<1>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
                        a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
-                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs);
+                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs, items);
   } else {
     const hipError_t e = set_lds(k_group_quantize<2>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_group_quantize<2>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
                        a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
-                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs);
+                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs, items);
   }
   return hipGetLastError();
 }

@@ -224,7 +224,7 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
  * launch; with GEMV groups, SwiGLU and the second quantization are one kernel.  A batch
  * of 1 to 32 assignments on the MFMA path has no grouping and no quantization launch: each
  * workgroup of the w13 GEMM groups the assignments and quantizes its group's source rows
- * itself (one of them writes the grouping's outputs to the workspace for the later
+ * itself (one more workgroup writes the grouping's outputs to the workspace for the later
  * launches), and each workgroup of the w2 GEMM quantizes its group's rows of h itself.  The w2 GEMM
  * writes each row's weighted scatter term, summed per token by the last launch.  The
  * results are bit-identical to calling the separate entry points in sequence.
@@ -288,7 +288,7 @@ int moe_layer_forward_noalloc(const moe_layer_desc* L, const uint16_t* x, int S,
  * epilogue, h = bf16( silu(g_gate[e] * acc_gate) * g_up[e] * acc_up ) (bf16 activations
  * carry no row global); the w2 GEMM over bf16 h; the scatter-add weighted by
  * row_w[i] * g_down[e].  A batch of 1 to 32 assignments has no grouping launch: each
- * workgroup of the w13 GEMM groups the assignments itself (one of them writes the
+ * workgroup of the w13 GEMM groups the assignments itself (one more workgroup writes the
  * grouping's outputs to the workspace), with the same results.
  * Same descriptor (flags and gemv_max_rows are not used: every group runs on the bf16
  * matrix cores), arguments, workspace (moe_layer_workspace_bytes) and error word as

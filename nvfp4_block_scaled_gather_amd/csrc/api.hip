@@ -360,10 +360,10 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
                                                  w.offsets, w.row_src, w.row_dst, w.row_w,
                                                  w.tok_off, w.tok_rows, w.err,
                                                  (const uint8_t*)L->w13_packed, I, H, L->g_gate,
-                                                 L->g_up, w.h16, stream, false);
+                                                 L->g_up, w.h16, stream, false, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: grouping w13 GEMM + SwiGLU launch");
     e = moe::launch_grouped_gemm_quantizing(w.h16, w.offsets, E, R, (const uint8_t*)L->w2_packed, H,
-                                            I, w.acc, w.row_w, L->g_down, stream);
+                                            I, w.acc, w.row_w, L->g_down, stream, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: quantizing w2 GEMM launch");
     e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
     return hip_status(e, "layer: scatter launch");
@@ -476,7 +476,7 @@ int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
                                                  w.offsets, w.row_src, w.row_dst, w.row_w,
                                                  w.tok_off, w.tok_rows, w.err,
                                                  (const uint8_t*)L->w13_packed, I, H, L->g_gate,
-                                                 L->g_up, w.h16, stream, true);
+                                                 L->g_up, w.h16, stream, true, nullptr);
     if (e != hipSuccess) return hip_status(e, "layer: W4A16 grouping w13 GEMM + SwiGLU launch");
   } else {
     e = moe::launch_group(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,

@@ -262,6 +262,12 @@ __device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], in
   if (t == 0) *gs_out = gs;
 }
 
+// The grouped GEMM's work list, written by the grouping: the non-empty groups in the order
+// the GEMM's items take them, groups of more than this many rows (one pass of activation
+// rows) first.  items[0] = {groups, groups of more than kWorkListMultiRows rows},
+// items[1 + a] = {expert, first grouped row, rows} of group a.
+constexpr int kWorkListMultiRows = 16;
+
 // ------------------------------------------------------------------ one-wave grouping
 // The grouping of a small batch (at most 64 assignments) by one wave, shared by the
 // grouping launch and the decode-sized w13 GEMM, which groups in every workgroup.
@@ -290,7 +296,8 @@ __device__ __forceinline__ void group_small(const int32_t* __restrict__ a_expert
                                             float* __restrict__ row_w,
                                             int32_t* __restrict__ tok_off,
                                             int32_t* __restrict__ tok_rows,
-                                            int32_t* __restrict__ err_word) {
+                                            int32_t* __restrict__ err_word,
+                                            int4* __restrict__ items = nullptr) {
   if (threadIdx.x >= 64) return;  // wave 0 only (no barrier follows)
   const int lane = threadIdx.x;
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -333,6 +340,24 @@ __device__ __forceinline__ void group_small(const int32_t* __restrict__ a_expert
     const int c = wave_count_below(skey, base + lane);
     if (base + lane <= E) expert_offsets[base + lane] = c;
   }
+  // 2b. the grouped GEMMs' work list (kWorkListMultiRows), when asked for: group sizes from
+  // the same counts, groups of more than kWorkListMultiRows rows first
+  if (items) {  // uniform
+    int n = 0, n_multi = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int base = 0; base < E; base += 64) {  // uniform
+        const int e = base + lane;
+        const int lo = wave_count_below(skey, e), hi = wave_count_below(skey, e + 1);
+        const int G = e < E ? hi - lo : 0;
+        const bool sel = pass == 0 ? G > kWorkListMultiRows : (G > 0 && G <= kWorkListMultiRows);
+        const uint64_t m = __ballot(sel);
+        if (sel) items[1 + n + __popcll(m & below)] = int4{e, lo, G, 0};
+        n += __popcll(m);
+      }
+      if (pass == 0) n_multi = n;
+    }
+    if (lane == 0) items[0] = int4{n, n_multi, 0, 0};
+  }
   // 3. token lists: valid rows in (output row, grouped position) order
   const int tkey = valid ? d * 64 + pos : 0x7FFFFFFF;
   int trank = 0;
@@ -349,12 +374,6 @@ __device__ __forceinline__ void group_small(const int32_t* __restrict__ a_expert
   for (int m = 32; m >= 1; m >>= 1) err |= __shfl_xor(err, m, 64);
   if (lane == 0) *err_word = err;
 }
-
-// The grouped GEMM's work list, written by the grouping: the non-empty groups in the order
-// the GEMM's items take them, groups of more than this many rows (one pass of activation
-// rows) first.  items[0] = {groups, groups of more than kWorkListMultiRows rows},
-// items[1 + a] = {expert, first grouped row, rows} of group a.
-constexpr int kWorkListMultiRows = 16;
 
 // Threads per row for NB scale blocks: a multiple of 64, at most 256.
 static inline int row_threads(int NB) {
@@ -407,8 +426,9 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* aq, const uint8_t* as, cons
                                       const int4* items = nullptr);
 // The same for a batch of 1..32 assignments, with the grouping of launch_group and the
 // quantization of the source rows x [S, K] done inside the launch (the grouping outputs are
-// written as launch_group writes them; the quantized rows stay in LDS).  bf16_acts: the
-// W4A16 arithmetic (launch_grouped_gemm_swiglu_w4a16), the rows used as bf16.
+// written as launch_group writes them, with the work list in items (E + 1 entries, or
+// nullptr); the quantized rows stay in LDS).  bf16_acts: the W4A16 arithmetic
+// (launch_grouped_gemm_swiglu_w4a16), the rows used as bf16.
 hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const int32_t* a_src,
                                                const int32_t* a_dst, const float* a_w, int R,
                                                int E, int S, int T, const uint16_t* x,
@@ -417,14 +437,16 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
                                                int32_t* tok_rows, int32_t* err_word,
                                                const uint8_t* w13, int I, int K,
                                                const float* g_gate, const float* g_up,
-                                               uint16_t* h, hipStream_t s, bool bf16_acts);
+                                               uint16_t* h, hipStream_t s, bool bf16_acts,
+                                               int4* items);
 // The w2 GEMM with the scatter-ready epilogue for a batch of 1..32 grouped rows, quantizing
 // its rows of h [R, K] (bf16, grouped order) itself: the bits of launch_quantize on h
-// followed by launch_grouped_gemm with c_gs = the quantized rows' globals.
+// followed by launch_grouped_gemm with c_gs = the quantized rows' globals.  items: the
+// work list launch_grouped_gemm_swiglu_grouping wrote for this batch, or nullptr.
 hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expert_offsets,
                                           int E, int R, const uint8_t* w2, int N, int K,
                                           float* out, const float* row_w, const float* g_down,
-                                          hipStream_t s);
+                                          hipStream_t s, const int4* items);
 // W4A16 (bf16 activation rows ab [a_rows, K], through amap): the grouped GEMM (with c_w,
 // rows multiplied by c_w[i] * c_g[e]) and the w13 GEMM with the SwiGLU epilogue (gate / up
 // globals alone).

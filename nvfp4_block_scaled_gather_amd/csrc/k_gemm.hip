@@ -628,7 +628,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
 // epilogue, every workgroup grouping the assignments itself with one wave (the one-wave
 // grouping's order) and quantizing its group's source rows straight into its staging area
 // with the grouping launch's quantizer, so the layer needs no grouping launch before this
-// one.  Workgroup 0 also writes the grouping's outputs for the later kernels.  The items,
+// one.  One extra workgroup writes the grouping's outputs for the later kernels.  The items,
 // passes and arithmetic are those of k_gemm_mfma's small-batch SwiGLU instance, so the
 // results are the same bits.  Workgroup ai / items_per_e takes the ai-th expert with rows
 // in ascending id (no multi-pass-first order: that only changes which workgroup computes
@@ -703,6 +703,7 @@ struct GroupArgs {
   int32_t* tok_off;
   int32_t* tok_rows;
   int32_t* err;
+  int4* items;  // the grouped GEMMs' work list for the later launches (or nullptr)
 };
 
 // ABF (W4A16): the source rows are bf16 activations used as they are (copied into the
@@ -722,10 +723,15 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
   const int tiles = p.I / 16, per_item = kGemmWaves;
   const int items_per_e = (tiles + per_item - 1) / per_item;
   const int ai = blockIdx.x / items_per_e;
+  if (blockIdx.x == gridDim.x - 1) {
+    // the launch's extra workgroup: the grouping's outputs for the later launches (the
+    // offsets, row maps and token lists, and the work list), off the items' path (measured
+    // on MI355X: a workgroup that also did this ended about 1 us after the others)
+    group_small(q.a_expert, q.a_src, q.a_dst, q.a_w, q.R, p.E, q.S, q.T, q.offsets, q.row_src,
+                q.row_dst, q.row_w, q.tok_off, q.tok_rows, q.err, q.items);
+    return;
+  }
   if (wave == 0) {
-    if (blockIdx.x == 0)
-      group_small(q.a_expert, q.a_src, q.a_dst, q.a_w, q.R, p.E, q.S, q.T, q.offsets, q.row_src,
-                  q.row_dst, q.row_w, q.tok_off, q.tok_rows, q.err);
     // grouped position of lane j's assignment: the number of (key, index) pairs below its
     // own (the counting loop with every lane active, as in group_small)
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -795,7 +801,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
     } else {
       auto rows = [&](int r) { return q.x + (size_t)s_src[b + r] * p.K; };
       if (b == 0) {  // one row at a time here: the ring's registers are live
-        // (half the ring: the other half's registers would cost occupancy at 4 tokens)
+        // (half the ring; issuing all of it here measured 0.9 us slower at one token)
         constexpr int P = D / 2 > 0 ? D / 2 : 1;
         quantize_rows_to_lds<BPT, 1>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, [&] {
           ring_prime<2, D, S, MOE_W_CPOL, P>(rg, wr, sstride, 16 * lane, S * 1024 + 2 * S * lane);
@@ -1138,14 +1144,16 @@ static hipError_t launch_swiglu_grouping_t(const int32_t* a_expert, const int32_
                                            int32_t* row_dst, float* row_w, int32_t* tok_off,
                                            int32_t* tok_rows, int32_t* err_word,
                                            const uint8_t* w13, int I, int K, const float* g_gate,
-                                           const float* g_up, uint16_t* h, hipStream_t s) {
+                                           const float* g_up, uint16_t* h, hipStream_t s,
+                                           int4* items) {
   if (R < 1 || R > kSmallGroupRows) return hipErrorInvalidValue;
   GemmArgs a{nullptr, nullptr, nullptr, S, expert_offsets, E, w13, 2 * I, K, nullptr, 1,
              0x7FFFFFFF, g_gate, g_up, nullptr, nullptr, h, I};
   const GroupArgs g{a_expert, a_src, a_dst, a_w, R, S, T, x, expert_offsets, row_src,
-                    row_dst, row_w, tok_off, tok_rows, err_word};
+                    row_dst, row_w, tok_off, tok_rows, err_word, items};
   const size_t lds = gemm_lds_bytes(K, ABF ? 4 : kPassRows, ABF);
-  const dim3 grid(gemm_grid(2 * kGemmWaves, a, R)), block(64 * kGemmWaves);
+  // one workgroup per item slot, plus the one that writes the grouping's outputs
+  const dim3 grid(gemm_grid(2 * kGemmWaves, a, R) + 1), block(64 * kGemmWaves);
   auto go = [&](auto kern) {
     if (lds > 65536) {
       const hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -1180,20 +1188,22 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
                                                int32_t* tok_rows, int32_t* err_word,
                                                const uint8_t* w13, int I, int K,
                                                const float* g_gate, const float* g_up,
-                                               uint16_t* h, hipStream_t s, bool bf16_acts) {
+                                               uint16_t* h, hipStream_t s, bool bf16_acts,
+                                               int4* items) {
   auto f = bf16_acts ? launch_swiglu_grouping_t<true> : launch_swiglu_grouping_t<false>;
   return f(a_expert, a_src, a_dst, a_w, R, E, S, T, x, expert_offsets, row_src, row_dst, row_w,
-           tok_off, tok_rows, err_word, w13, I, K, g_gate, g_up, h, s);
+           tok_off, tok_rows, err_word, w13, I, K, g_gate, g_up, h, s, items);
 }
 
 hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expert_offsets,
                                           int E, int R, const uint8_t* w2, int N, int K,
                                           float* out, const float* row_w, const float* g_down,
-                                          hipStream_t s) {
+                                          hipStream_t s, const int4* items) {
   if (R < 1 || R > kSmallGroupRows) return hipErrorInvalidValue;
   GemmArgs a{nullptr, nullptr, nullptr, R, expert_offsets, E, w2, N, K, out, 1, 0x7FFFFFFF};
   a.c_w = row_w;
   a.c_g = g_down;
+  a.items = items;
   const size_t lds = gemm_lds_bytes(K, kPassRows, false, 1);
   const dim3 grid(gemm_grid(kGemmWaves, a, R)), block(64 * kGemmWaves);
   auto go = [&](auto kern) {

@@ -476,23 +476,23 @@ int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
                                                  w.offsets, w.row_src, w.row_dst, w.row_w,
                                                  w.tok_off, w.tok_rows, w.err,
                                                  (const uint8_t*)L->w13_packed, I, H, L->g_gate,
-                                                 L->g_up, w.h16, stream, true, nullptr);
+                                                 L->g_up, w.h16, stream, true, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: W4A16 grouping w13 GEMM + SwiGLU launch");
   } else {
     e = moe::launch_group(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
-                          w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, stream);
+                          w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, stream, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: group launch");
     if (R > 0) {
       e = moe::launch_grouped_gemm_swiglu_w4a16(x, w.row_src, S, w.offsets, E, R,
                                                 (const uint8_t*)L->w13_packed, I, H, L->g_gate,
-                                                L->g_up, w.h16, stream);
+                                                L->g_up, w.h16, stream, w.items);
       if (e != hipSuccess) return hip_status(e, "layer: W4A16 w13 GEMM + SwiGLU launch");
     }
   }
   if (R > 0) {
     e = moe::launch_grouped_gemm_w4a16(w.h16, nullptr, R, w.offsets, E, R,
                                        (const uint8_t*)L->w2_packed, H, I, w.acc, stream, w.row_w,
-                                       L->g_down);
+                                       L->g_down, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: W4A16 w2 GEMM launch");
   }
   e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);

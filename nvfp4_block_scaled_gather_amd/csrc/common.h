@@ -386,12 +386,15 @@ static inline int row_threads(int NB) {
 // ------------------------------------------------------------------ internal launchers
 // (host functions defined in the kernel translation units; arguments already validated)
 namespace moe {
+// Grouping of the assignments (moe_gather_rows without the gather); items (E + 1 entries,
+// or nullptr): also the grouped GEMM's work list (kWorkListMultiRows).
 hipError_t launch_pack(const uint8_t* nib, const uint8_t* scl, int E, int N, int K, uint8_t* packed,
                        bool unpack, uint8_t* nib_out, uint8_t* scl_out, hipStream_t s);
 hipError_t launch_group(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
                         const float* a_w, int R, int E, int S, int T, int32_t* expert_offsets,
                         int32_t* row_src, int32_t* row_dst, float* row_w, int32_t* tok_off,
-                        int32_t* tok_rows, int32_t* err_word, hipStream_t s);
+                        int32_t* tok_rows, int32_t* err_word, hipStream_t s,
+                        int4* items = nullptr);
 hipError_t launch_gather(const uint16_t* x, int H, const int32_t* row_src, int R, uint16_t* xg,
                          hipStream_t s);
 // Output row i quantizes input row row_map[i] (row_map == nullptr: row i); rows at or past
@@ -453,11 +456,13 @@ hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expe
 hipError_t launch_grouped_gemm_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
                                      const int32_t* expert_offsets, int E, int R, const uint8_t* w,
                                      int N, int K, float* out, hipStream_t s,
-                                     const float* c_w = nullptr, const float* c_g = nullptr);
+                                     const float* c_w = nullptr, const float* c_g = nullptr,
+                                     const int4* items = nullptr);
 hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
                                             const int32_t* expert_offsets, int E, int R,
                                             const uint8_t* w13, int I, int K, const float* g_gate,
-                                            const float* g_up, uint16_t* h, hipStream_t s);
+                                            const float* g_up, uint16_t* h, hipStream_t s,
+                                            const int4* items = nullptr);
 // Grouping and NVFP4 quantization of the S source rows of x in one launch (independent
 // work: block 0 groups, the other blocks quantize four rows each).  items (E + 1 entries,
 // or nullptr): for more than 32 assignments, also the grouped GEMM's work list (see

@@ -1103,11 +1103,12 @@ static bool small_w4a16(const GemmArgs& a, int R) { return small_grid(a, R) && R
 hipError_t launch_grouped_gemm_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
                                      const int32_t* off, int E, int R, const uint8_t* w, int N,
                                      int K, float* out, hipStream_t s, const float* c_w,
-                                     const float* c_g) {
+                                     const float* c_g, const int4* items) {
   GemmArgs a{nullptr, nullptr, amap, a_rows, off, E, w, N, K, out, 1, 0x7FFFFFFF};
   a.c_w = c_w;
   a.c_g = c_g;
   a.ab = ab;
+  a.items = items;  // (read only by the instances that stage kWorkListMultiRows rows a pass)
   if (small_w4a16(a, R))
     return launch_mfma_t<1, 8, false, true, kGemmWaves, kSmallW4A16PassRows>(a, kGemmWaves, R, s);
   // Up to K = 2048 the 16 staged rows take at most 64 KiB: two workgroups of 8 waves per CU,
@@ -1120,10 +1121,11 @@ hipError_t launch_grouped_gemm_w4a16(const uint16_t* ab, const int32_t* amap, in
 hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* amap, int a_rows,
                                             const int32_t* off, int E, int R, const uint8_t* w13,
                                             int I, int K, const float* g_gate, const float* g_up,
-                                            uint16_t* h, hipStream_t s) {
+                                            uint16_t* h, hipStream_t s, const int4* items) {
   GemmArgs a{nullptr, nullptr, amap, a_rows, off, E, w13, 2 * I, K, nullptr, 1, 0x7FFFFFFF,
              g_gate, g_up, nullptr, nullptr, h, I};
   a.ab = ab;
+  a.items = items;  // (as above)
   // one gate tile per wave: (I/WAVES)/16 items per expert, the grid of N = 2I with 2 WAVES
   // tiles per item
   if (small_w4a16(a, R))

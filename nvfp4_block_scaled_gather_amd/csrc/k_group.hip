@@ -297,17 +297,17 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(
     const int32_t* __restrict__ a_dst, const float* __restrict__ a_w, int R, int E, int S, int T,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ row_src, int32_t* __restrict__ row_dst,
     float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
-    int32_t* __restrict__ err_word, bool parallel, bool cached) {
+    int32_t* __restrict__ err_word, bool parallel, bool cached, int4* __restrict__ items) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   if (R <= kSmallGroupRows)
     group_small(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w,
-                tok_off, tok_rows, err_word);
+                tok_off, tok_rows, err_word, items);
   else if (cached)
     group_body<true>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
-                     row_w, tok_off, tok_rows, err_word, parallel, lds);
+                     row_w, tok_off, tok_rows, err_word, parallel, lds, items);
   else
     group_body<false>(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
-                      row_w, tok_off, tok_rows, err_word, parallel, lds);
+                      row_w, tok_off, tok_rows, err_word, parallel, lds, items);
 }
 
 // Grouping (block 0) and NVFP4 quantization of the S source rows of x (the other blocks,
@@ -382,14 +382,14 @@ static hipError_t set_lds(Kern kern, size_t lds) {
 hipError_t launch_group(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
                         const float* a_w, int R, int E, int S, int T, int32_t* expert_offsets,
                         int32_t* row_src, int32_t* row_dst, float* row_w, int32_t* tok_off,
-                        int32_t* tok_rows, int32_t* err_word, hipStream_t s) {
+                        int32_t* tok_rows, int32_t* err_word, hipStream_t s, int4* items) {
   const bool par = group_parallel(E, T), cached = group_cached(E, T, R);
   const size_t lds = R <= kSmallGroupRows ? 0 : group_lds_ints(E, T, par, R, cached) * sizeof(int);
   const hipError_t e = set_lds(k_group, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupThreads), lds, s, a_expert, a_src, a_dst, a_w, R,
                      E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off, tok_rows, err_word,
-                     par, cached);
+                     par, cached, items);
   return hipGetLastError();
 }
 

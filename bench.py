@@ -430,7 +430,7 @@ def w4a16_leg(args, weights):
     """The W4A16 mode (moe_layer_forward_w4a16: bf16 activations against the same resident
     NVFP4 weights, the pages' GEMV arithmetic) on ragged570 and ragged2303, timed like the
     main leg (graph replays after the settle), and on decode M = 1, 8, 32 like the M sweep
-    (cache flush before each call).  Also the largest difference between the W4A16 and
+    (cache flush before each call; the faster of graph replay and eager launches).  Also the largest difference between the W4A16 and
     W4A4 layer outputs on ragged570, relative to the W4A16 row RMS (informational: two
     different arithmetics, [GG] "Numbers")."""
     import torch
@@ -472,23 +472,29 @@ def w4a16_leg(args, weights):
         dl = L.DeviceLayer(wl, weights=weights, arithmetic="w4a16")
         graph = dl.capture_graph()
 
-        def step():
-            dst.copy_(src)
-            graph.replay()
+        def timed(run):
+            def step():
+                dst.copy_(src)
+                run()
 
-        warm(step, args.warmup, args.settle_ms)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for a, b in ev:
-            dst.copy_(src)
-            a.record()
-            graph.replay()
-            b.record()
-        torch.cuda.synchronize()
-        med = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            warm(step, args.warmup, args.settle_ms)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a, b in ev:
+                dst.copy_(src)
+                a.record()
+                run()
+                b.record()
+            torch.cuda.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+        g_med, e_med = timed(graph.replay), timed(dl.forward)
+        med, launch = (g_med, "hip-graph replay") if g_med <= e_med else (e_med, "eager")
         n_act = len(wl.active_experts())
         wbytes = n_act * LAYER_BYTES_PER_EXPERT
-        pts.append({"M": M, "layer_us": med * 1e3, "weight_GBps": wbytes / (med * 1e-3) / 1e9,
+        pts.append({"M": M, "layer_us": med * 1e3, "launch": launch,
+                    "layer_us_graph": g_med * 1e3, "layer_us_eager": e_med * 1e3,
+                    "weight_GBps": wbytes / (med * 1e-3) / 1e9,
                     "frac_of_hbm_peak": wbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS})
         log(json.dumps({"w4a16_decode": pts[-1]}))
         del graph, dl

@@ -79,6 +79,27 @@ def test_layer_equals_separate_calls(lib, flags, gemv_max):
     assert np.array_equal(got, composed_layer(B, dl, flags, gemv_max))
 
 
+@pytest.mark.parametrize("name,E,H,I", [("zipf512", 24, 1536, 768), ("zipf512", 40, 1024, 512),
+                                        ("ragged2303", 16, 4096, 2048)])
+def test_layer_multi_pass_groups_equal_separate_calls(lib, name, E, H, I):
+    """Groups of 17 to ~170 rows (two to eleven 16-row passes over the same weights, the
+    passes of an item in one workgroup, multi-pass groups first in the work list) at 12, 8
+    and 32 items per expert: the layer is bit-identical to the separate entry points, which
+    find their groups by scanning the offsets."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("multi-pass groups vs separate calls", name, E, H, I)
+    wl = W.make_workload(name, E=E, H=H, I=I)
+    sizes = np.bincount(wl.a_expert, minlength=E)
+    assert (sizes > 16).any()
+    dl = L.DeviceLayer(wl, flags=0, gemv_max_rows=0)
+    got = host(dl.forward())
+    sync()
+    assert dl.device_error() == 0
+    assert np.array_equal(got, composed_layer(B, dl, 0, 0))
+
+
 @pytest.mark.parametrize("R,hot", [(1, 0), (17, 17), (32, 20), (33, 20)])
 def test_decode_sized_layer_equals_separate_calls(lib, R, hot):
     """Batches of at most 32 assignments take the w13 launch that groups and quantizes by

@@ -111,11 +111,21 @@ __host__ __device__ __forceinline__ int b_stride(int K) { return 2 * K + 16; }
 // The staging area also holds the MFMA epilogue's output block (16 rows x the workgroup's
 // columns plus padding), which for small K is larger than the staged rows; 256 bytes of
 // slack keep the B-operand prefetch past the last chunk inside the allocation.
-static size_t out_block_bytes(int NS, int waves) { return (size_t)kPassRows * (16 * NS * waves + 4) * 4; }
+static size_t out_block_bytes(int NS, int waves, int rows = kPassRows) {
+  return (size_t)rows * (16 * NS * waves + 4) * 4;
+}
+// A double pass (mfma_dpass) stages kDPassRows rows over half of K at a time.
+constexpr int kDPassRows = 2 * kPassRows;
 static size_t gemm_lds_bytes(int K, int rows, bool abf = false, int NS = 2,
                              int waves = kGemmWaves) {
-  const size_t stage = (size_t)rows * (abf ? b_stride(K) : q_stride(K) + s_stride(K));
-  const size_t outb = out_block_bytes(NS, waves);
+  size_t stage = (size_t)rows * (abf ? b_stride(K) : q_stride(K) + s_stride(K));
+  size_t outb = out_block_bytes(NS, waves);
+  if (!abf && rows == kPassRows) {  // the instances that run double passes
+    const size_t dstage = (size_t)kDPassRows * (q_stride(K / 2) + s_stride(K / 2));
+    const size_t dout = out_block_bytes(NS, waves, kDPassRows);
+    stage = stage > dstage ? stage : dstage;
+    outb = outb > dout ? outb : dout;
+  }
   return (stage > outb ? stage : outb) + 256;
 }
 
@@ -398,6 +408,87 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pass_weights(const GemmArgs& p
   return make_rsrc(wt, __builtin_amdgcn_readfirstlane(range));
 }
 
+// The pass's epilogue.  Lane l holds output rows r + 16 hr (hr < HR) x weight rows
+// 4 kq .. 4 kq + 3 of each tile in acc[hr].  The workgroup's output block (its rows x
+// 16 NS WAVES columns, or x 16 WAVES h columns) is assembled in LDS over the staged rows and
+// written as whole rows, so every store covers full 128-byte lines (written from the lanes
+// directly, each line arrived in 32- or 64-byte pieces from several waves).  ow / ogs:
+// lane row r + 16 hr's router weight and activation global (scatter-ready epilogue); FQ:
+// the row globals are s_rgs[row] instead.
+template <int NS, int HR, bool SWI, bool ABF, int WAVES, bool FQ>
+__device__ __forceinline__ void pass_epilogue(const GemmArgs& p, const f32x4 (&acc)[HR][NS],
+                                              int nsv, int arow0, int nrows, int col0,
+                                              uint8_t* s_q, float ggate, float gup,
+                                              const float* s_rgs, const float (&ow)[HR],
+                                              const float (&ogs)[HR]) {
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, r = lane & 15;
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();  // every wave is done with the staged rows: reuse them for the output
+  if (SWI) {
+    constexpr int WCH = 16 * WAVES;            // h columns of the workgroup
+    constexpr int LPR = WCH / 8;               // 16-byte pieces per row
+    uint16_t* so = (uint16_t*)s_q;             // [rows][WCH + 8] bf16 (the output block)
+#pragma unroll
+    for (int hr = 0; hr < HR; ++hr) {
+      const int rr = r + kPassRows * hr;
+      if (rr < nrows && nsv > 0) {
+        const int i = arow0 + rr;
+        const float gs = FQ ? s_rgs[rr] : p.row_gs ? p.row_gs[p.gs_map ? p.gs_map[i] : i] : 1.0f;
+        const float cg = gs * ggate, cu = gs * gup;
+        uint32_t hb[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) hb[x] = swiglu_bf16(cg, acc[hr][0][x], cu, acc[hr][1][x]);
+        const u32x2 v = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        *(u32x2*)(so + rr * (WCH + 8) + wave * 16 + 4 * kq) = v;
+      }
+    }
+    __syncthreads();
+    const int colW = col0 - 16 * wave;
+    const __amdgpu_buffer_rsrc_t ho = make_rsrc(p.h + (size_t)arow0 * p.I, nrows * p.I * 2);
+    for (int u = threadIdx.x; u < nrows * LPR; u += 64 * WAVES) {
+      const int row = u / LPR, c = (u % LPR) * 8;
+      if (colW + c < p.I) {
+        const u32x4 v = *(const u32x4*)(so + row * (WCH + 8) + c);
+        store_out<ABF>(v, ho, (row * p.I + colW + c) * 2);
+      }
+    }
+  } else {
+    constexpr int WC = 16 * NS * WAVES;        // the workgroup's output columns
+    constexpr int LPR = WC / 4;                // 16-byte pieces per row
+    float* so = (float*)s_q;                   // [rows][WC + 4] floats (the output block)
+#pragma unroll
+    for (int hr = 0; hr < HR; ++hr) {
+      const int rr = r + kPassRows * hr;
+      if (rr < nrows) {
+        // ggate: the expert's down global here; FQ: the row global just computed
+        const float cf = ow[hr] * ggate * (FQ ? s_rgs[rr] : ogs[hr]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          f32x4 v = acc[hr][s];
+          if (p.c_w) {
+            v[0] = v[0] * cf;
+            v[1] = v[1] * cf;
+            v[2] = v[2] * cf;
+            v[3] = v[3] * cf;
+          }
+          if (s < nsv) *(f32x4*)(so + rr * (WC + 4) + wave * 16 * NS + 16 * s + 4 * kq) = v;
+        }
+      }
+    }
+    __syncthreads();
+    const int colW = col0 - 16 * NS * wave;
+    const __amdgpu_buffer_rsrc_t oo = make_rsrc(p.out + (size_t)arow0 * p.N, nrows * p.N * 4);
+    for (int u = threadIdx.x; u < nrows * LPR; u += 64 * WAVES) {
+      const int row = u / LPR, c = (u % LPR) * 4;
+      if (colW + c < p.N) {
+        const f32x4 v = *(const f32x4*)(so + row * (WC + 4) + c);
+        store_out<ABF>(__builtin_bit_cast(u32x4, v), oo, (row * p.N + colW + c) * 4);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------- MFMA path
 // One pass: stage the pass's rows, then stream NS weight tiles (wt: first tile, uniform)
 // against them.  Every wave of the workgroup calls this together (it synchronizes); a
@@ -457,9 +548,9 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   }
 
   const int rl = r < nrows ? r : 0;
-  f32x4 acc[NS];
+  f32x4 acc[1][NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < NS; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if constexpr (ABF) {
     // W4A16: the B operand is the staged bf16 row as it is, with the weights' k
@@ -485,8 +576,8 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bf16x8 aop = dequant8_bf16(wn[s][q], q >= 2 ? f1 : f0);
-          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bq[q]),
-                                                           acc[s], 0, 0, 0);
+          acc[0][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              aop, __builtin_bit_cast(bf16x8, bq[q]), acc[0][s], 0, 0, 0);
         }
       }
     }, rg);
@@ -514,81 +605,136 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f16x8 aop = dequant8(wn[s][q], sw, q >= 2);
-          acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[q], acc[s], 0, 0, 0);
+          acc[0][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[q], acc[0][s], 0, 0, 0);
         }
       }
     }, rg);
   }
 
-  // Lane l holds out row r x weight rows 4 kq .. 4 kq + 3 of each tile.  The workgroup's
-  // output block (its rows x 16 NS WAVES columns, or x 16 WAVES h columns) is assembled in
-  // LDS over the staged rows and written as whole rows, so every store covers full
-  // 128-byte lines (written from the lanes directly, each line arrived in 32- or 64-byte
-  // pieces from several waves).
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();  // every wave is done with the staged rows: reuse them for the output
-  if (SWI) {
-    constexpr int WCH = 16 * WAVES;            // h columns of the workgroup
-    constexpr int LPR = WCH / 8;               // 16-byte pieces per row
-    uint16_t* so = (uint16_t*)s_q;             // [16][WCH + 8] bf16 (within the output block)
-    if (r < nrows && nsv > 0) {
-      const int i = arow0 + r;
-      const float gs = FQ ? s_rgs[r] : p.row_gs ? p.row_gs[p.gs_map ? p.gs_map[i] : i] : 1.0f;
-      const float cg = gs * ggate, cu = gs * gup;
-      uint32_t hb[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) hb[x] = swiglu_bf16(cg, acc[0][x], cu, acc[1][x]);
-      const u32x2 v = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-      *(u32x2*)(so + r * (WCH + 8) + wave * 16 + 4 * kq) = v;
+  const float ow1[1] = {ow}, ogs1[1] = {ogs};
+  pass_epilogue<NS, 1, SWI, ABF, WAVES, FQ>(p, acc, nsv, arow0, nrows, col0, s_q, ggate, gup, s_rgs,
+                                           ow1, ogs1);
+}
+
+// Stage K-half hf (columns [hf K/2, (hf + 1) K/2)) of NVFP4 rows arow0 .. arow0 + nrows - 1
+// into LDS as rows of K/2 columns (row strides q_stride(K/2) and s_stride(K/2)).
+template <int WAVES>
+__device__ __forceinline__ void stage_rows_half(const GemmArgs& p, int arow0, int nrows, int hf,
+                                                uint8_t* s_q, uint8_t* s_s) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qb = p.K / 2, sb = p.K / 16, hq = qb / 2, hs = sb / 2, K2 = p.K / 2;
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.aq, p.a_rows * qb);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.as, p.a_rows * sb);
+  for (int row = wave; row < nrows; row += WAVES) {
+    const int i = arow0 + row;
+    const int src = __builtin_amdgcn_readfirstlane(p.amap ? p.amap[i] : i);
+    uint8_t* dq = s_q + row * q_stride(K2);
+    uint8_t* ds = s_s + row * s_stride(K2);
+    for (int o = 0; o < hq; o += 1024) {
+      if (o + 16 * lane < hq)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(dq + o), 16, 16 * lane,
+                                                 src * qb + hf * hq + o, 0, 0);
     }
-    __syncthreads();
-    const int colW = col0 - 16 * wave;
-    const __amdgpu_buffer_rsrc_t ho = make_rsrc(p.h + (size_t)arow0 * p.I, nrows * p.I * 2);
-    for (int u = threadIdx.x; u < nrows * LPR; u += 64 * WAVES) {
-      const int row = u / LPR, c = (u % LPR) * 8;
-      if (colW + c < p.I) {
-        const u32x4 v = *(const u32x4*)(so + row * (WCH + 8) + c);
-        store_out<ABF>(v, ho, (row * p.I + colW + c) * 2);
-      }
-    }
-  } else {
-    constexpr int WC = 16 * NS * WAVES;        // the workgroup's output columns
-    constexpr int LPR = WC / 4;                // 16-byte pieces per row
-    float* so = (float*)s_q;                   // [16][WC + 4] floats (the output block)
-    if (r < nrows) {
-      // ggate: the expert's down global here; FQ: the row global just computed
-      const float cf = ow * ggate * (FQ ? s_rgs[r] : ogs);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        f32x4 v = acc[s];
-        if (p.c_w) {
-          v[0] = v[0] * cf;
-          v[1] = v[1] * cf;
-          v[2] = v[2] * cf;
-          v[3] = v[3] * cf;
-        }
-        if (s < nsv) *(f32x4*)(so + r * (WC + 4) + wave * 16 * NS + 16 * s + 4 * kq) = v;
-      }
-    }
-    __syncthreads();
-    const int colW = col0 - 16 * NS * wave;
-    const __amdgpu_buffer_rsrc_t oo = make_rsrc(p.out + (size_t)arow0 * p.N, nrows * p.N * 4);
-    for (int u = threadIdx.x; u < nrows * LPR; u += 64 * WAVES) {
-      const int row = u / LPR, c = (u % LPR) * 4;
-      if (colW + c < p.N) {
-        const f32x4 v = *(const f32x4*)(so + row * (WC + 4) + c);
-        store_out<ABF>(__builtin_bit_cast(u32x4, v), oo, (row * p.N + colW + c) * 4);
-      }
+    for (int o = 0; o < hs; o += 256) {
+      if (o + 4 * lane < hs)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(ds + o), 4, 4 * lane,
+                                                 src * sb + hf * hs + o, 0, 0);
     }
   }
+}
+
+// A double pass (NVFP4 activations, groups of more than kPassRows rows): up to kDPassRows
+// rows against one stream of the NS weight tiles, the rows staged over one half of K at a
+// time (the LDS of one pass of kPassRows rows over all of K), lane row r taking rows r and
+// r + 16 as two B operands, each MFMA of a chunk issued once per operand.  Every output
+// accumulates over the chunks in mfma_pass's order with the same instructions, so the
+// results are the bits of two single passes, with the weights streamed once instead of
+// twice.  Needs an even number of scale groups (K / 128 a multiple of 2 S), so that each
+// half starts a scale group.  The B operands are read from LDS in the chunk that uses them
+// (no read-ahead): the two operands' registers keep the instance within 128 registers per
+// lane, four waves per SIMD.
+template <int NS, int D, int S, bool SWI, int WAVES, int WPOL>
+__device__ __forceinline__ void mfma_dpass(const GemmArgs& p, const uint8_t* __restrict__ wt,
+                                           int nsv, int arow0, int nrows, int col0,
+                                           uint8_t* s_q, float ggate, float gup) {
+  static_assert(!SWI || NS == 2, "the SwiGLU epilogue pairs one gate and one up tile");
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, r = lane & 15;
+  const int K2 = p.K / 2, NC2 = p.K / 256;
+  uint8_t* s_s = s_q + kDPassRows * q_stride(K2);
+  asm volatile("" ::: "memory");  // (as in mfma_pass: no loads hoisted across passes)
+  int sstride;
+  const int tstride = (p.K / 128) * kChunkBytes;
+  sstride = SWI ? (p.I / 16) * tstride : tstride;
+  const int range = nsv <= 0 ? 0 : SWI ? sstride + tstride : nsv * tstride;
+  const int hoff = (NC2 / S) * S * kChunkBytes;  // the second half: its first scale group
+  float ow[2] = {0.f, 0.f}, ogs[2] = {1.f, 1.f};
+#pragma unroll
+  for (int hr = 0; hr < 2; ++hr) {
+    const int rr = r + kPassRows * hr;
+    if (!SWI && p.c_w && rr < nrows) {
+      ow[hr] = p.c_w[arow0 + rr];
+      if (p.c_gs) ogs[hr] = p.c_gs[arow0 + rr];
+    }
+  }
+  // lanes past the pass's rows read row 0: their B columns only feed rows not stored
+  const int rl0 = r < nrows ? r : 0;
+  const int rl1 = r + kPassRows < nrows ? r + kPassRows : 0;
+  f32x4 acc[2][NS];
+#pragma unroll
+  for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[hr][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hf = 0; hf < 2; ++hf) {
+    if (hf) __syncthreads();  // every wave is done with the first half's rows
+    stage_rows_half<WAVES>(p, arow0, nrows, hf, s_q, s_s);
+    __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
+    __syncthreads();
+    const int hrange = range == 0 ? 0 : hf ? range - hoff : range;
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(wt + (hf ? hoff : 0), __builtin_amdgcn_readfirstlane(hrange));
+    Ring<NS, D> rg;
+    const uint8_t* aq0 = s_q + rl0 * q_stride(K2) + 16 * kq;
+    const uint8_t* aq1 = s_q + rl1 * q_stride(K2) + 16 * kq;
+    const uint8_t* as0 = s_s + rl0 * s_stride(K2) + 2 * kq;
+    const uint8_t* as1 = s_s + rl1 * s_stride(K2) + 2 * kq;
+    stream_weights_c<NS, D, S, WPOL>(wr, NC2, sstride, 16 * lane, S * 1024 + 2 * S * lane,
+                             [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
+      const u32x4 an0 = *(const u32x4*)(aq0 + 64 * c), an1 = *(const u32x4*)(aq1 + 64 * c);
+      const uint32_t sa0 = scale_pair_signed(*(const uint16_t*)(as0 + 8 * c));
+      const uint32_t sa1 = scale_pair_signed(*(const uint16_t*)(as1 + 8 * c));
+      uint32_t sw[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        sw[s] = scale_pair_pos(sg[s][j >> 1], (j & 1) ? 0x0c030c02u : 0x0c010c00u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f16x8 b0 = dequant8(an0[q], sa0, q >= 2);
+        const f16x8 b1 = dequant8(an1[q], sa1, q >= 2);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const f16x8 aop = dequant8(wn[s][q], sw[s], q >= 2);
+          acc[0][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, b0, acc[0][s], 0, 0, 0);
+          acc[1][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, b1, acc[1][s], 0, 0, 0);
+        }
+      }
+    }, rg);
+  }
+  pass_epilogue<NS, 2, SWI, false, WAVES, false>(p, acc, nsv, arow0, nrows, col0, s_q, ggate,
+                                                 gup, nullptr, ow, ogs);
 }
 
 // One workgroup per item: item it covers tiles [ii * per_item, (ii + 1) * per_item) of active
 // group it / items_per_e (ii = it % items_per_e).  The grid has one item slot per group
 // that can be non-empty, so every item has a workgroup and no workgroup has two.
-// PR: activation rows staged per pass (at most the B operand's 16 columns).
+// PR: activation rows staged per pass (at most the B operand's 16 columns).  Groups of
+// more than PR rows take double passes where they can (mfma_dpass); the waves-per-SIMD
+// hint keeps the 4-chunk-ring NVFP4 instances at four waves per SIMD with the double
+// pass's registers (without it they compile to three).
 template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, int PR>
-__global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(ABF || D > 4 ? 1 : 4)))
+void k_gemm_mfma(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_grp[4];
   uint8_t* s_q = smem;
@@ -609,7 +755,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mfma(GemmArgs p) {
   const float ggate = SWI ? p.g_gate[g.e] : p.c_w ? p.c_g[g.e] : 0.f;
   const float gup = SWI ? p.g_up[g.e] : 0.f;
   if (g.G > PR) {  // uniform: several passes over the same weights
-    for (int b = 0; b < g.G; b += PR) {
+    int b = 0;
+    if constexpr (!ABF && PR == kPassRows) {
+      // double passes while more than one pass's rows remain (an even number of scale
+      // groups; uniform)
+      if ((p.K / 128) % (2 * S) == 0) {
+        for (; g.G - b > PR; b += kDPassRows) {
+          if (b) __syncthreads();  // the previous pass is done with the staged rows
+          mfma_dpass<NS, D, S, SWI, WAVES, kMultiPassWCpol>(
+              p, wt, nsv, g.r0 + b, min(kDPassRows, g.G - b), 16 * t0, s_q, ggate, gup);
+        }
+      }
+    }
+    for (; b < g.G; b += PR) {
       if (b) __syncthreads();  // the previous pass is done with the staged rows
       mfma_pass<NS, D, S, SWI, ABF, WAVES, false, kMultiPassWCpol>(
           p, wt, nsv, g.r0 + b, min(PR, g.G - b), 16 * t0, s_q, s_s, ggate, gup);

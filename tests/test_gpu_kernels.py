@@ -421,6 +421,38 @@ def test_gemm_row_invariance_within_path(lib, flags, sizes):
         assert np.array_equal(grouped.view(np.uint32), alone[:g].view(np.uint32)), g
 
 
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_gemm_double_passes_equal_single_rows_and_oracle(lib, K):
+    """Groups of more than 16 rows at a K with an even number of scale groups take double
+    passes (up to 32 rows against one stream of the weights, staged over half of K at a
+    time), the rest of a group single passes: every output within the GEMM tolerance of the
+    oracle, and the rows at each pass boundary equal to the same rows computed alone, bit
+    for bit ([GG] "Proof": a row's output does not depend on its group)."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    say("gemm double passes", K)
+    rng = np.random.default_rng(130 + K // 1024)
+    N = 256
+    sizes = [17, 25, 32, 33, 40, 57, 64, 65, 3]
+    E = len(sizes)
+    off = offsets_from_sizes(sizes)
+    aq, as_ = _workload_like(rng, int(off[-1]), K)
+    wn, wsc = rand_nvfp4(rng, E * N, K, 0x20, 0x40)
+    wp = pack(B, wn, wsc, E, N, K)
+    got = run_gemm(B, aq, as_, off, wp, N, K, 2, gemv_max=0)
+    want = _oracle_gemm(aq, as_, off, wn, wsc, E, N, K)
+    rms = np.sqrt(np.mean(want ** 2, axis=1, keepdims=True))
+    assert np.all(np.abs(got - want) <= GEMM_TOL * rms), float((np.abs(got - want) / rms).max())
+    for e, g in enumerate(sizes):
+        for k in sorted({0, 15, 16, 31, 32, 47, 48, 63, 64, g - 1}):
+            if k >= g:
+                continue
+            r = int(off[e]) + k
+            alone = run_gemm(B, aq[r:r + 1], as_[r:r + 1],
+                             offsets_from_sizes([0] * e + [1] + [0] * (E - e - 1)), wp, N, K, 2,
+                             gemv_max=0)
+            assert np.array_equal(alone.view(np.uint32), got[r:r + 1].view(np.uint32)), (e, k)
+
+
 @pytest.mark.parametrize("flags", [0, 2])
 def test_gemm_grid_paths_agree_bitwise(lib, flags):
     """A small batch (few non-empty groups: the deep-ring, one-tile-per-wave instance) and a

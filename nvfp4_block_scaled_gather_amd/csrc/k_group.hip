@@ -20,6 +20,7 @@ namespace moe {
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / 64;
 constexpr int kSmallGroupRows = 32;  // group_small: at most one assignment per lane
+constexpr int kWorkListUnits = 256;  // units of 64 experts of the work list's two sets
 
 // Lanes of the wave whose `key` equals this lane's key (keys < 2^bits).
 __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits, bool active) {
@@ -32,6 +33,20 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits, bool activ
   return active ? m : 0ull;
 }
 
+// Inclusive prefix sum of v over the 64 lanes of a wave: a scan within each row of 16
+// lanes by row shifts (lanes shifted in from outside the row add 0), then the totals of
+// the rows below (read from their last lanes) added to each row.  Every lane must call it.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 // Exclusive scan of cnt[0..n) in place by the whole workgroup; returns the total.
 __device__ __forceinline__ int block_exclusive_scan(int* cnt, int n, int* s_part) {
   const int tid = threadIdx.x;
@@ -41,19 +56,11 @@ __device__ __forceinline__ int block_exclusive_scan(int* cnt, int n, int* s_part
   for (int k = lo; k < hi; ++k) local += cnt[k];
   // inclusive scan of the per-thread sums across the block (wave scan + wave totals)
   const int lane = tid & 63, wave = tid >> 6;
-  int v = local;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  const int v = wave_scan_incl(local);
   if (lane == 63) s_part[wave] = v;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kGroupWaves ? s_part[lane] : 0;
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(w, d, 64);
-      if (lane >= d) w += o;
-    }
+    const int w = wave_scan_incl(lane < kGroupWaves ? s_part[lane] : 0);
     if (lane < kGroupWaves) s_part[lane] = w;  // inclusive wave prefix
   }
   __syncthreads();
@@ -72,7 +79,8 @@ __device__ __forceinline__ int block_exclusive_scan(int* cnt, int n, int* s_part
 // bucket_start[key] (an exclusive prefix of the key counts; used as scratch).
 // With nw = 16 waves, wave w owns the contiguous segment [w*seg, (w+1)*seg): per-wave key
 // histograms (hist, 16 x nkeys ints of LDS) turn the bucket starts into per-(wave, key)
-// cursors.  With nw = 1, wave 0 walks all items and bucket_start itself is the cursor.
+// cursors (hist_zeroed: the caller cleared those 16 x nkeys ints already, before a barrier).
+// With nw = 1, wave 0 walks all items and bucket_start itself is the cursor.
 // Inside a wave items go 64 at a time; a lane's rank is the number of equal-key lanes
 // below it.  With `masks` (nw x nkeys 64-bit words of LDS, zero on entry and on return)
 // the lanes OR their bit into their key's word and read it back (OR is order-free, so the
@@ -82,23 +90,29 @@ __device__ __forceinline__ int block_exclusive_scan(int* cnt, int n, int* s_part
 template <typename KeyFn, typename PlaceFn>
 __device__ __forceinline__ void stable_place(int n, int nkeys, int* bucket_start, int* hist, int nw,
                                              KeyFn key_of, PlaceFn place,
-                                             unsigned long long* masks = nullptr) {
+                                             unsigned long long* masks = nullptr,
+                                             bool hist_zeroed = false) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = (n + nw - 1) / nw;
   const int j0 = wave < nw ? wave * seg : n, j1 = min(n, j0 + seg);
   int* h = bucket_start;
   if (nw > 1) {
     h = hist + wave * nkeys;
-    for (int k = tid; k < nw * nkeys; k += kGroupThreads) hist[k] = 0;
-    __syncthreads();
+    if (!hist_zeroed) {
+      for (int k = tid; k < nw * nkeys; k += kGroupThreads) hist[k] = 0;
+      __syncthreads();
+    }
     for (int j = j0 + lane; j < j1; j += 64) atomicAdd(&h[key_of(j)], 1);
     __syncthreads();
-    for (int b = tid; b < nkeys; b += kGroupThreads) {
+    for (int b = tid; b < nkeys; b += kGroupThreads) {  // (nw == kGroupWaves here)
+      int c[kGroupWaves];
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) c[w] = hist[w * nkeys + b];  // all reads first
       int run = bucket_start[b];
-      for (int w = 0; w < nw; ++w) {
-        const int c = hist[w * nkeys + b];
+#pragma unroll
+      for (int w = 0; w < kGroupWaves; ++w) {
         hist[w * nkeys + b] = run;
-        run += c;
+        run += c[w];
       }
     }
     __syncthreads();
@@ -179,6 +193,8 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
   for (int k = tid; k < T + 1; k += kGroupThreads) cnt_t[k] = 0;
   if (CACHED)
     for (int k = tid; k < nw * nkmax; k += kGroupThreads) masks[k] = 0ull;
+  if (parallel)  // the expert placement's per-wave histograms (stable_place, hist_zeroed)
+    for (int k = tid; k < nw * (E + 1); k += kGroupThreads) hist[k] = 0;
   if (tid == 0) s_err = 0;
   __syncthreads();
   // 1. validate and count (four assignments' loads in flight per thread)
@@ -234,23 +250,56 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
   // 2b. the GEMMs' work list (when asked for): the non-empty groups in the order the grouped
   // GEMM takes them, groups of more than kWorkListMultiRows rows first, each set in ascending
   // expert id; items[0] = {groups, groups of the first set}, items[1 + a] = {expert, first
-  // row, rows} of group a.  With it a GEMM workgroup finds its group with one load instead of
-  // a scan of the offsets.  Wave 0 alone, from the offsets in LDS.
-  if (items && tid < 64) {
-    const uint64_t below = tid ? (~0ull >> (64 - tid)) : 0ull;
-    int n = 0, n_multi = 0;
-    for (int pass = 0; pass < 2; ++pass) {
-      for (int base = 0; base < E; base += 64) {  // uniform
-        const int e = base + tid;
-        const int G = e < E ? cnt_e[e + 1] - cnt_e[e] : 0;
-        const bool sel = pass == 0 ? G > kWorkListMultiRows : (G > 0 && G <= kWorkListMultiRows);
-        const uint64_t m = __ballot(sel);
-        if (sel) items[1 + n + __popcll(m & below)] = int4{e, cnt_e[e], G, 0};
-        n += __popcll(m);
-      }
-      if (pass == 0) n_multi = n;
+  // row, rows, a} of group a.  With it a GEMM workgroup finds its group with one load
+  // instead of a scan of the offsets.  From the offsets in LDS, by all waves: unit u of the
+  // list is 64 experts of one set (u < nb: the first set, experts 64 u ..; then the second),
+  // wave w takes units w, w + 16, ...: one ballot counts a unit's groups, a barrier, then
+  // each wave places its units' groups after the counts of the units before them.
+  if (items) {  // uniform
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int nb = (E + 63) / 64, nu = 2 * nb;  // nu <= kWorkListUnits (E <= 8192)
+    __shared__ int s_cnt[kWorkListUnits];
+    auto unit_sel = [&](int u, int& e) {
+      const int set = u / nb;
+      e = (u - set * nb) * 64 + lane;
+      const int G = e < E ? cnt_e[e + 1] - cnt_e[e] : 0;
+      return set == 0 ? G > kWorkListMultiRows : (G > 0 && G <= kWorkListMultiRows);
+    };
+    for (int u = wave; u < nu; u += kGroupWaves) {
+      int e;
+      const int c = __popcll(__ballot(unit_sel(u, e)));
+      if (lane == 0) s_cnt[u] = c;
     }
-    if (tid == 0) items[0] = int4{n, n_multi, 0, 0};
+    __syncthreads();
+    // the units' exclusive prefix: one scan over the wave when there are at most 64 units
+    // (E <= 2048), else sums of the counts read from LDS
+    int incl = 0, total = 0, n_multi = 0;
+    if (nu <= 64) {  // uniform
+      incl = wave_scan_incl(lane < nu ? s_cnt[lane] : 0);
+      total = __builtin_amdgcn_readlane(incl, 63);
+      n_multi = __builtin_amdgcn_readlane(incl, nb - 1);
+    } else {
+      for (int u = 0; u < nu; ++u) {
+        total += s_cnt[u];
+        if (u == nb - 1) n_multi = total;
+      }
+    }
+    for (int u = wave; u < nu; u += kGroupWaves) {
+      int before;
+      if (nu <= 64) {
+        before = __builtin_amdgcn_readlane(incl, u) - s_cnt[u];
+      } else {
+        before = 0;
+        for (int v = 0; v < u; ++v) before += s_cnt[v];
+      }
+      int e;
+      const bool sel = unit_sel(u, e);
+      const uint64_t m = __ballot(sel);
+      const int a = before + __popcll(m & below);
+      if (sel) items[1 + a] = int4{e, cnt_e[e], cnt_e[e + 1] - cnt_e[e], a};
+    }
+    if (tid == 0) items[0] = int4{total, n_multi, 0, 0};
   }
   __syncthreads();
   // 3. grouped rows in (expert, assignment) order; dropped assignments last
@@ -261,7 +310,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
                    g_src[pos] = ok ? c_src[j] : -1;
                    g_dst[pos] = ok ? c_dst[j] : -1;
                    g_w[pos] = ok ? c_w[j] : 0.f;
-                 }, masks);
+                 }, masks, parallel);
     for (int i = tid; i < R; i += kGroupThreads) {  // (after stable_place's barrier)
       row_src[i] = g_src[i];
       row_dst[i] = g_dst[i];
@@ -278,7 +327,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ a_expert,
       row_src[pos] = ok ? a_src[j] : -1;
       row_dst[pos] = ok ? a_dst[j] : -1;
       row_w[pos] = ok ? a_w[j] : 0.f;
-    });
+    }, nullptr, parallel);
   }
   // 4. token lists, ascending grouped row (the grouped rows' outputs are visible after
   // stable_place's barrier)
@@ -362,7 +411,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_quantize(
 
 // LDS of the grouping workgroup: per-wave histograms when they fit in 64 KiB; the cached
 // assignments on top when the total fits in the CU's 160 KiB.
-constexpr size_t kGroupLdsMax = 159 * 1024;  // the CU's 160 KiB less the static LDS
+constexpr size_t kGroupLdsMax = 158 * 1024;  // the CU's 160 KiB less the static LDS
 
 static bool group_parallel(int E, int T) {
   return group_lds_ints(E, T, true, 0, false) * sizeof(int) <= 65536;

@@ -800,12 +800,15 @@ constexpr int kSmallGroupRows = 32;
 // the workgroup takes part).  after_first_loads() runs
 // once, after the first rows' loads are issued and before they are waited for (the caller
 // issues its first weight loads there, so that their latency overlaps the quantization;
-// loads complete in order, so they must come after the rows' loads).  The caller
-// synchronizes before the staged rows are read.
-template <int BPT, int RPS, class RowPtr, class AfterLoads>
+// loads complete in order, so they must come after the rows' loads).  PRE: pre holds this
+// thread's BPT blocks of a row the caller loaded already, used for every row (all rows the
+// same source row; otherwise pre is not read).  The caller synchronizes before the staged
+// rows are read.
+template <int BPT, int RPS, bool PRE = false, class RowPtr, class AfterLoads>
 __device__ __forceinline__ void quantize_rows_to_lds(RowPtr row_ptr, int nrows, int K,
                                                      uint8_t* s_q, uint8_t* s_s, float* s_rgs,
-                                                     float* s_red, AfterLoads after_first_loads) {
+                                                     float* s_red, AfterLoads after_first_loads,
+                                                     const u32x4 (&pre)[BPT][2]) {
   constexpr int NT = 64 * kGemmWaves;  // threads per row: block b = t + NT k of each row
   const int NB = K / 16, t = threadIdx.x;
   for (int r = 0; r < nrows; r += RPS) {
@@ -817,7 +820,10 @@ __device__ __forceinline__ void quantize_rows_to_lds(RowPtr row_ptr, int nrows, 
       for (int k = 0; k < BPT; ++k) {
         const int blk = t + NT * k;
         w[rr][k][0] = w[rr][k][1] = u32x4{0u, 0u, 0u, 0u};
-        if (src && blk < NB) {
+        if constexpr (PRE) {  // every row is the one whose blocks the caller loaded
+          w[rr][k][0] = pre[k][0];
+          w[rr][k][1] = pre[k][1];
+        } else if (src && blk < NB) {
           const u32x4* px = (const u32x4*)(src + 16 * blk);
           w[rr][k][0] = px[0];
           w[rr][k][1] = px[1];
@@ -847,6 +853,15 @@ __device__ __forceinline__ void quantize_rows_to_lds(RowPtr row_ptr, int nrows, 
   }
 }
 
+template <int BPT, int RPS, class RowPtr, class AfterLoads>
+__device__ __forceinline__ void quantize_rows_to_lds(RowPtr row_ptr, int nrows, int K,
+                                                     uint8_t* s_q, uint8_t* s_s, float* s_rgs,
+                                                     float* s_red, AfterLoads after_first_loads) {
+  const u32x4 none[BPT][2] = {};
+  quantize_rows_to_lds<BPT, RPS, false>(row_ptr, nrows, K, s_q, s_s, s_rgs, s_red,
+                                        after_first_loads, none);
+}
+
 struct GroupArgs {
   const int32_t* a_expert;
   const int32_t* a_src;
@@ -866,7 +881,7 @@ struct GroupArgs {
 
 // ABF (W4A16): the source rows are bf16 activations used as they are (copied into the
 // staging area, row global 1), in passes of 4 rows like the small-batch W4A16 instance.
-template <int D, int S, bool ABF, int BPT>
+template <int D, int S, bool ABF, int BPT, bool PRE = false>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmArgs p, GroupArgs q) {
   constexpr int PR = ABF ? 4 : kPassRows;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -881,6 +896,23 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
   const int tiles = p.I / 16, per_item = kGemmWaves;
   const int items_per_e = (tiles + per_item - 1) / per_item;
   const int ai = blockIdx.x / items_per_e;
+  // PRE (one source row, a single decode token; NVFP4): every grouped row is that row, so
+  // its blocks are loaded now and arrive while wave 0 groups.  A separate instance: the
+  // registers they hold would cost the general one a wave per SIMD.
+  static_assert(!PRE || !ABF, "the prefetch feeds the NVFP4 quantization");
+  u32x4 xpre[BPT][2];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int blk = threadIdx.x + 64 * kGemmWaves * k;
+      xpre[k][0] = xpre[k][1] = u32x4{0u, 0u, 0u, 0u};
+      if (blk < p.K / 16) {
+        const u32x4* px = (const u32x4*)(q.x + 16 * blk);
+        xpre[k][0] = px[0];
+        xpre[k][1] = px[1];
+      }
+    }
+  }
   if (blockIdx.x == gridDim.x - 1) {
     // the launch's extra workgroup: the grouping's outputs for the later launches (the
     // offsets, row maps and token lists, and the work list), off the items' path (measured
@@ -961,9 +993,13 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
       if (b == 0) {  // one row at a time here: the ring's registers are live
         // (half the ring; issuing all of it here measured 0.9 us slower at one token)
         constexpr int P = D / 2 > 0 ? D / 2 : 1;
-        quantize_rows_to_lds<BPT, 1>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, [&] {
+        auto prime = [&] {
           ring_prime<2, D, S, MOE_W_CPOL, P>(rg, wr, sstride, 16 * lane, S * 1024 + 2 * S * lane);
-        });
+        };
+        if constexpr (PRE)
+          quantize_rows_to_lds<BPT, 1, true>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, prime, xpre);
+        else
+          quantize_rows_to_lds<BPT, 1>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, prime);
         mfma_pass<2, D, S, true, false, kGemmWaves, true, MOE_W_CPOL, P>(
             p, wt, nsv, r0 + b, nrows, 16 * t0, s_q, s_s, ggate, gup, s_rgs, &rg);
       } else {
@@ -1324,6 +1360,14 @@ static hipError_t launch_swiglu_grouping_t(const int32_t* a_expert, const int32_
     return hipGetLastError();
   };
   // (a thread quantizes one 16-element block of each row up to K = 4096, two above)
+  if (K <= 64 * kGemmWaves * 16 && !ABF && S == 1) {  // one source row: its prefetching instance
+    switch (scale_group(K / 128)) {
+      case 8: return go(k_gemm_swiglu_grouping<8, 8, false, 1, true>);
+      case 4: return go(k_gemm_swiglu_grouping<4, 4, false, 1, true>);
+      case 2: return go(k_gemm_swiglu_grouping<2, 2, false, 1, true>);
+      default: return go(k_gemm_swiglu_grouping<1, 1, false, 1, true>);
+    }
+  }
   if (K <= 64 * kGemmWaves * 16) {
     switch (scale_group(K / 128)) {
       case 8: return go(k_gemm_swiglu_grouping<8, 8, ABF, 1>);

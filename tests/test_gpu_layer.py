@@ -128,6 +128,35 @@ def test_decode_sized_layer_equals_separate_calls(lib, R, hot):
     assert np.array_equal(got, composed_layer(B, dl, 0, 0))
 
 
+@pytest.mark.parametrize("R,hot", [(1, 0), (8, 0), (20, 18)])
+def test_single_source_row_layer_equals_separate_calls(lib, R, hot):
+    """One source row (a single decode token): the decode-sized w13 launch takes the
+    instance that loads the row's blocks before it groups; bit-identical to the separate
+    entry points, with one group of 18 rows of that row (two passes: the first from the
+    loaded blocks, the second loading them again) and two dropped assignments."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("single-source-row layer vs separate calls", R, hot)
+    base = W.make_workload("ragged2303", E=24, H=512, I=256)
+    a_expert = (np.arange(R) % base.E).astype(np.int32)
+    a_expert[:hot] = 5
+    a_src = np.zeros(R, np.int32)
+    a_dst = np.zeros(R, np.int32)
+    if R >= 8:
+        a_expert[3] = base.E    # expert id out of range
+        a_src[4] = 1            # source row out of range
+    a_w = np.linspace(0.1, 1.0, R).astype(np.float32)
+    wl = W.Workload(**{**base.__dict__, "x": base.x[:1], "S": 1, "T": 1, "a_expert": a_expert,
+                       "a_src": a_src, "a_dst": a_dst, "a_w": a_w})
+    dl = L.DeviceLayer(wl, flags=0, gemv_max_rows=0)
+    got = host(dl.forward())
+    sync()
+    err = dl.device_error()
+    assert err == (0 if R < 8 else B.MOE_ERR_EXPERT | B.MOE_ERR_SRC), err
+    assert np.array_equal(got, composed_layer(B, dl, 0, 0))
+
+
 @pytest.mark.parametrize("flags", [1, 2])
 def test_layer_batch_parity_and_determinism(lib, flags):
     """[GG] "Proof" / batch parity: a token's output is the same

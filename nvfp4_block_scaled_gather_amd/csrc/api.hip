@@ -363,7 +363,7 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
                                                  L->g_up, w.h16, stream, false, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: grouping w13 GEMM + SwiGLU launch");
     e = moe::launch_grouped_gemm_quantizing(w.h16, w.offsets, E, R, (const uint8_t*)L->w2_packed, H,
-                                            I, w.acc, w.row_w, L->g_down, stream, w.items);
+                                            I, w.acc, w.row_w, L->g_down, stream, w.items, S == 1);
     if (e != hipSuccess) return hip_status(e, "layer: quantizing w2 GEMM launch");
     e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
     return hip_status(e, "layer: scatter launch");

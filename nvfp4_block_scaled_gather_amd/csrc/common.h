@@ -445,11 +445,13 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
 // The w2 GEMM with the scatter-ready epilogue for a batch of 1..32 grouped rows, quantizing
 // its rows of h [R, K] (bf16, grouped order) itself: the bits of launch_quantize on h
 // followed by launch_grouped_gemm with c_gs = the quantized rows' globals.  items: the
-// work list launch_grouped_gemm_swiglu_grouping wrote for this batch, or nullptr.
+// work list launch_grouped_gemm_swiglu_grouping wrote for this batch, or nullptr;
+// one_source: the batch has a single source row (its groups are then one row each as a
+// rule, which the launch uses to load rows of h early).
 hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expert_offsets,
                                           int E, int R, const uint8_t* w2, int N, int K,
                                           float* out, const float* row_w, const float* g_down,
-                                          hipStream_t s, const int4* items);
+                                          hipStream_t s, const int4* items, bool one_source = false);
 // W4A16 (bf16 activation rows ab [a_rows, K], through amap): the grouped GEMM (with c_w,
 // rows multiplied by c_w[i] * c_g[e]) and the w13 GEMM with the SwiGLU epilogue (gate / up
 // globals alone).

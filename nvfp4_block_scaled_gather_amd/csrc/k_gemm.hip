@@ -1017,7 +1017,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_swiglu_grouping(GemmAr
 // quantization launch between the two GEMMs; the scatter coefficient takes the row global
 // it has just computed.  Items, passes and arithmetic are those of k_gemm_mfma's
 // small-batch instance: the same bits.
-template <int D, int S, int BPT>
+template <int D, int S, int BPT, bool PRE = false>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_quantizing(GemmArgs p,
                                                                      const uint16_t* __restrict__ h) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -1029,8 +1029,26 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_quantizing(GemmArgs p,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tiles = p.N / 16, per_item = kGemmWaves;  // one tile per wave
   const int items_per_e = (tiles + per_item - 1) / per_item;
+  const int ai = blockIdx.x / items_per_e;
+  // PRE (one source row, a single decode token): its experts are distinct as a rule, so
+  // every group is one row and group ai is grouped row ai; that row's blocks are loaded
+  // before the group is known and used if the group proves to be that row.  A separate
+  // instance, for the registers they hold (as in k_gemm_swiglu_grouping).
+  u32x4 hpre[BPT][2];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int blk = threadIdx.x + 64 * kGemmWaves * k;
+      hpre[k][0] = hpre[k][1] = u32x4{0u, 0u, 0u, 0u};
+      if (ai < p.a_rows && blk < p.K / 16) {
+        const u32x4* px = (const u32x4*)(h + (size_t)ai * p.K + 16 * blk);
+        hpre[k][0] = px[0];
+        hpre[k][1] = px[1];
+      }
+    }
+  }
   ItemGroup g;
-  if (!find_group<kPassRows>(p, blockIdx.x / items_per_e, s_grp, g)) return;  // uniform
+  if (!find_group<kPassRows>(p, ai, s_grp, g)) return;  // uniform
   const int t0 = (blockIdx.x % items_per_e) * per_item + wave;
   const int nsv = min(1, tiles - t0);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
@@ -1048,9 +1066,13 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_quantizing(GemmArgs p,
     const int row0 = g.r0 + b;
     auto rows = [&](int r) { return h + (size_t)(row0 + r) * p.K; };
     if (b == 0) {  // one row at a time here: the ring's registers are live
-      quantize_rows_to_lds<BPT, 1>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, [&] {
+      auto prime = [&] {
         ring_prime<1, D, S, MOE_W_CPOL>(rg, wr, sstride, 16 * lane, S * 1024 + 2 * S * lane);
-      });
+      };
+      if (PRE && g.G == 1 && g.r0 == ai)  // uniform: the row loaded at entry is the group's
+        quantize_rows_to_lds<BPT, 1, true>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, prime, hpre);
+      else
+        quantize_rows_to_lds<BPT, 1>(rows, nrows, p.K, s_q, s_s, s_rgs, s_red, prime);
       mfma_pass<1, D, S, false, false, kGemmWaves, true, MOE_W_CPOL, D>(
           p, wt, nsv, row0, nrows, 16 * t0, s_q, s_s, gdown, 0.f, s_rgs, &rg);
     } else {
@@ -1402,7 +1424,7 @@ hipError_t launch_grouped_gemm_swiglu_grouping(const int32_t* a_expert, const in
 hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expert_offsets,
                                           int E, int R, const uint8_t* w2, int N, int K,
                                           float* out, const float* row_w, const float* g_down,
-                                          hipStream_t s, const int4* items) {
+                                          hipStream_t s, const int4* items, bool one_source) {
   if (R < 1 || R > kSmallGroupRows) return hipErrorInvalidValue;
   GemmArgs a{nullptr, nullptr, nullptr, R, expert_offsets, E, w2, N, K, out, 1, 0x7FFFFFFF};
   a.c_w = row_w;
@@ -1419,6 +1441,14 @@ hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expe
     hipLaunchKernelGGL(kern, grid, block, lds, s, a, h);
     return hipGetLastError();
   };
+  if (K <= 64 * kGemmWaves * 16 && one_source) {  // its prefetching instance
+    switch (scale_group(K / 128)) {
+      case 8: return go(k_gemm_quantizing<8, 8, 1, true>);
+      case 4: return go(k_gemm_quantizing<4, 4, 1, true>);
+      case 2: return go(k_gemm_quantizing<2, 2, 1, true>);
+      default: return go(k_gemm_quantizing<1, 1, 1, true>);
+    }
+  }
   if (K <= 64 * kGemmWaves * 16) {
     switch (scale_group(K / 128)) {
       case 8: return go(k_gemm_quantizing<8, 8, 1>);

@@ -55,15 +55,15 @@ __device__ __forceinline__ uint32_t e2m1x8_encode(const float* q) {
 }
 
 // Eight e2m1 nibbles (one 32-bit word, element 2k in the low nibble of byte k) times a
-// non-negative block scale given as a float -> 8 exact bf16 values in element order (W4A16
-// weights).  Each nibble pair converts to float exactly, the product with the e4m3 scale
-// has at most 6 significant bits (exact in float), and its upper 16 bits are then the bf16
-// value itself.
+// non-negative block scale given as a float times 2^-8 (scale_pair_pos's f16 halves,
+// widened) -> 8 exact bf16 values in element order (W4A16 weights).  Each nibble pair
+// converts to float times 2^8 exactly, the product with the scaled e4m3 value has at most
+// 6 significant bits (exact in float), and its upper 16 bits are then the bf16 value itself.
 __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t w, float scale) {
-  const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 0);
+  const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 1);
+  const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 2);
+  const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 256.0f, 3);
   const f32x2 pp[4] = {p0, p1, p2, p3};
   u32x4 r;
 #pragma unroll

@@ -571,8 +571,10 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
       __builtin_amdgcn_sched_barrier(0);  // issue the reads before this chunk's work
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const uint32_t ws = chunk_scales(sg[s], j);
-        const float f0 = e4m3_to_f32(ws & 0xFFu), f1 = e4m3_to_f32(ws >> 8);
+        // the chunk's two block scales times 2^-8 (exact f16, widened exactly)
+        const f16x2 hs = __builtin_bit_cast(
+            f16x2, scale_pair_pos(sg[s][j >> 1], (j & 1) ? 0x0c030c02u : 0x0c010c00u));
+        const float f0 = (float)hs[0], f1 = (float)hs[1];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const bf16x8 aop = dequant8_bf16(wn[s][q], q >= 2 ? f1 : f0);

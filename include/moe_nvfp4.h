@@ -225,9 +225,11 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
  * of 1 to 32 assignments on the MFMA path has no grouping and no quantization launch: each
  * workgroup of the w13 GEMM groups the assignments and quantizes its group's source rows
  * itself (one more workgroup writes the grouping's outputs to the workspace for the later
- * launches), and each workgroup of the w2 GEMM quantizes its group's rows of h itself.  The w2 GEMM
- * writes each row's weighted scatter term, summed per token by the last launch.  The
- * results are bit-identical to calling the separate entry points in sequence.
+ * launches), and each workgroup of the w2 GEMM quantizes its group's rows of h itself.
+ * The w2 GEMM writes each row's weighted scatter term, summed per token by the last launch;
+ * with at most 16 assignments (and I <= 1024 or I = 2048; also I = 3072 or 4096 with at
+ * most 8 assignments) the w2 launch sums each token's terms itself, and the layer is two
+ * launches.  The results are bit-identical to calling the separate entry points in sequence.
  *
  * L (host): E, H, I; w13_packed (E x [2I, H], gate rows first) and w2_packed
  *   (E x [H, I]) from nvfp4_pack_weights; per-expert globals g_gate, g_up, g_down [E];

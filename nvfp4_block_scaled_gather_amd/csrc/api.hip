@@ -354,14 +354,22 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
     // A decode-sized batch on the MFMA path, three launches: the w13 GEMM launch groups the
     // assignments and quantizes its rows by itself (writing h to its own buffer, since the
     // w2 launch reads h while writing its terms into acc), the w2 GEMM launch quantizes h
-    // by itself, then the per-token sum.  Measured on MI355X to save the two small
-    // launches' time at one to four tokens; the same bits as the sequence below.
+    // by itself, then the per-token sum; up to 16 rows the w2 launch sums the tokens too.
+    // Measured on MI355X to save the small launches' time at one to four tokens; the same
+    // bits as the sequence below.
     e = moe::launch_grouped_gemm_swiglu_grouping(a_expert, a_src, a_dst, a_w, R, E, S, T, x,
                                                  w.offsets, w.row_src, w.row_dst, w.row_w,
                                                  w.tok_off, w.tok_rows, w.err,
                                                  (const uint8_t*)L->w13_packed, I, H, L->g_gate,
                                                  L->g_up, w.h16, stream, false, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: grouping w13 GEMM + SwiGLU launch");
+    if (moe::grouped_gemm_quantizing_sum_fits(R, I)) {
+      // at most 16 rows: the w2 launch also sums each token's terms (two launches in all)
+      e = moe::launch_grouped_gemm_quantizing_sum(w.h16, E, R, (const uint8_t*)L->w2_packed, H,
+                                                  I, w.row_w, L->g_down, w.items, w.tok_off,
+                                                  w.tok_rows, T, out, stream);
+      return hip_status(e, "layer: quantizing w2 GEMM + per-token sum launch");
+    }
     e = moe::launch_grouped_gemm_quantizing(w.h16, w.offsets, E, R, (const uint8_t*)L->w2_packed, H,
                                             I, w.acc, w.row_w, L->g_down, stream, w.items, S == 1);
     if (e != hipSuccess) return hip_status(e, "layer: quantizing w2 GEMM launch");

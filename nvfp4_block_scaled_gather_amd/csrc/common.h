@@ -452,6 +452,16 @@ hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expe
                                           int E, int R, const uint8_t* w2, int N, int K,
                                           float* out, const float* row_w, const float* g_down,
                                           hipStream_t s, const int4* items, bool one_source = false);
+// A batch of at most 16 expert-rows: the w2 GEMM of launch_grouped_gemm_quantizing and the
+// per-token sum of launch_token_sum in one launch (no scatter terms in global memory), the
+// same bits; items: the work list launch_grouped_gemm_swiglu_grouping wrote (required).
+// grouped_gemm_quantizing_sum_fits: whether the launch takes R rows at this K.
+bool grouped_gemm_quantizing_sum_fits(int R, int K);
+hipError_t launch_grouped_gemm_quantizing_sum(const uint16_t* h, int E, int R, const uint8_t* w2,
+                                              int N, int K, const float* row_w,
+                                              const float* g_down, const int4* items,
+                                              const int32_t* tok_off, const int32_t* tok_rows,
+                                              int T, uint16_t* out, hipStream_t s);
 // W4A16 (bf16 activation rows ab [a_rows, K], through amap): the grouped GEMM (with c_w,
 // rows multiplied by c_w[i] * c_g[e]) and the w13 GEMM with the SwiGLU epilogue (gate / up
 // globals alone).

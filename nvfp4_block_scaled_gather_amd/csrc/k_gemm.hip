@@ -490,6 +490,47 @@ __device__ __forceinline__ void pass_epilogue(const GemmArgs& p, const f32x4 (&a
 }
 
 // ------------------------------------------------------------------------- MFMA path
+// The NVFP4 MFMA loop of a pass, for kernels whose waves run passes of their own (the
+// decode-sized w2 launch that also sums the tokens): streams the NS weight tiles of wr
+// against staged activation row rl (this lane's B column; K columns, staging area s_q /
+// s_s), accumulating into acc, with the instructions of mfma_pass's NVFP4 loop (kept inline
+// there: calling this from mfma_pass changed its address arithmetic and measured 0.6 us
+// slower at one decode token).  The B operand of chunk c is read from LDS while chunk c - 1
+// is computed (reads one chunk past the end land in the row padding, the next region or
+// the slack: never used).
+template <int NS, int D, int S, int WPOL, int PRIMED>
+__device__ __forceinline__ void nvfp4_stream_mfma(__amdgpu_buffer_rsrc_t wr, int K, int sstride,
+                                                  const uint8_t* s_q, const uint8_t* s_s, int rl,
+                                                  f32x4 (&acc)[NS], Ring<NS, D>& rg) {
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, NC = K / 128;
+  const uint8_t* aq_l = s_q + rl * q_stride(K) + 16 * kq;
+  const uint8_t* as_l = s_s + rl * s_stride(K) + 2 * kq;
+  u32x4 an_next = *(const u32x4*)aq_l;
+  uint32_t asc_next = *(const uint16_t*)as_l;
+  stream_weights_c<NS, D, S, WPOL, PRIMED>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
+                           [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
+    const u32x4 an = an_next;
+    const uint32_t asc = asc_next;
+    an_next = *(const u32x4*)(aq_l + 64 * (c + 1));
+    asc_next = *(const uint16_t*)(as_l + 8 * (c + 1));
+    __builtin_amdgcn_sched_barrier(0);  // issue the reads before this chunk's work
+    const uint32_t sa = scale_pair_signed(asc);
+    f16x8 bop[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bop[q] = dequant8(an[q], sa, q >= 2);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint32_t sw = scale_pair_pos(sg[s][j >> 1], (j & 1) ? 0x0c030c02u : 0x0c010c00u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f16x8 aop = dequant8(wn[s][q], sw, q >= 2);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[q], acc[s], 0, 0, 0);
+      }
+    }
+  }, rg);
+}
+
 // One pass: stage the pass's rows, then stream NS weight tiles (wt: first tile, uniform)
 // against them.  Every wave of the workgroup calls this together (it synchronizes); a
 // wave with no tile in this item (nsv <= 0) loads nothing (empty buffer range) and stores
@@ -1085,6 +1126,173 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_gemm_quantizing(GemmArgs p,
   }
 }
 
+// A batch of at most WV expert-rows (one or two decode tokens): the w2 GEMM and the per-token
+// sum in one launch.  Workgroup c owns output columns 16 c .. 16 c + 15 of every token:
+// wave w takes group w of the work list (one 16-row tile of that expert's w2 weights,
+// streamed over all of K), quantizes the group's rows of h into the staging area itself,
+// and puts each row's scatter term (the product times row_w[i] * g_down[e] * hgs[i], in
+// the order of the scatter-ready epilogue) into LDS; after one barrier the workgroup sums
+// each token's terms as the per-token sum does (eight interleaved partial sums over the
+// token's list, added in order 0..7) and writes the token's 16 bf16 outputs.  No term
+// goes through global memory and there is no third launch.  A wave quantizes its rows
+// alone (the row maximum by a wave reduction); every product, term and sum is the
+// operation the separate launches perform, so the output has the same bits.
+struct TokenSumArgs {
+  const int32_t* tok_off;   // [T + 1]
+  const int32_t* tok_rows;  // grouped rows of token t: tok_rows[tok_off[t] .. tok_off[t + 1])
+  int T;
+  uint16_t* out;            // [T, N] bf16
+};
+constexpr int kSumTokLds = 64;  // tokens whose list offsets are read into LDS at entry
+
+template <int WV, int D, int S, int BPT>
+__global__ __launch_bounds__(64 * WV) void k_gemm_quantizing_sum(GemmArgs p,
+                                                                 const uint16_t* __restrict__ h,
+                                                                 TokenSumArgs ts) {
+  static_assert(WV == 8 || WV == 16, "a power of two of at most 16 waves");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float s_rgs[WV];       // row globals of the grouped rows
+  __shared__ f32x4 s_term[WV][4];   // scatter terms: [grouped row][4 columns x 4]
+  __shared__ int s_rows[WV];        // the token lists
+  __shared__ int s_off[kSumTokLds + 1];
+  const int K = p.K, R = p.a_rows, NB = K / 16;
+  uint8_t* s_q = smem;                      // [WV rows][q_stride(K)]
+  uint8_t* s_s = s_q + WV * q_stride(K);    // [WV rows][s_stride(K)], then 256 bytes of slack
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = blockIdx.x;
+  // grouped row `wave` of h, loaded before the work list arrives: when every group is one
+  // row (distinct experts, the rule for one token), group `wave` is that row
+  u32x4 hpre[BPT][2];
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int blk = lane + 64 * k;
+    hpre[k][0] = hpre[k][1] = u32x4{0u, 0u, 0u, 0u};
+    if (wave < R && blk < NB) {
+      const u32x4* px = (const u32x4*)(h + (size_t)wave * K + 16 * blk);
+      hpre[k][0] = px[0];
+      hpre[k][1] = px[1];
+    }
+  }
+  // the token lists, for the sum at the end (put into LDS after the GEMM, so that no wave
+  // waits for them before its weight loads)
+  const int tr = threadIdx.x < R ? ts.tok_rows[threadIdx.x] : 0;
+  const int to = threadIdx.x <= min(ts.T, kSumTokLds) ? ts.tok_off[threadIdx.x] : 0;
+  // this wave's group: work list entry `wave` (ascending expert id; R <= WV <= 16 rows, so
+  // no group takes a second pass)
+  int4 it = int4{0, 0, 0, 0};
+  if (wave < R && wave < p.E) it = p.items[1 + wave];
+  const int ng = __builtin_amdgcn_readfirstlane(p.items[0].x);
+  const bool has = wave < ng;  // uniform
+  const int e = has ? __builtin_amdgcn_readfirstlane(it.x) : 0;
+  const int r0 = has ? __builtin_amdgcn_readfirstlane(it.y) : 0;
+  const int G = has ? __builtin_amdgcn_readfirstlane(it.z) : 0;
+  const size_t expert_bytes = (size_t)p.N * K / 16 * 9;
+  const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)tile * 9 * K;
+  int sstride;
+  const __amdgpu_buffer_rsrc_t wr = pass_weights<false>(p, wt, has ? 1 : 0, sstride);
+  Ring<1, D> rg;
+  float ow = 0.f, gdown = 0.f;
+  const int kq = lane >> 4, rr = lane & 15;
+  if (has) {
+    ring_prime<1, D, S, MOE_W_CPOL>(rg, wr, sstride, 16 * lane, S * 1024 + 2 * S * lane);
+    gdown = p.c_g[e];
+    if (rr < G) ow = p.c_w[r0 + rr];
+    // the group's rows of h, quantized by this wave alone
+    for (int r = 0; r < G; ++r) {
+      const int i = r0 + r;
+      u32x4 w[BPT][2];
+      const bool pre = G == 1 && r0 == wave;  // uniform: the row loaded at entry
+#pragma unroll
+      for (int k = 0; k < BPT; ++k) {
+        const int blk = lane + 64 * k;
+        w[k][0] = hpre[k][0];
+        w[k][1] = hpre[k][1];
+        if (!pre) {
+          w[k][0] = w[k][1] = u32x4{0u, 0u, 0u, 0u};
+          if (blk < NB) {
+            const u32x4* px = (const u32x4*)(h + (size_t)i * K + 16 * blk);
+            w[k][0] = px[0];
+            w[k][1] = px[1];
+          }
+        }
+      }
+      float v[BPT][16];
+#pragma unroll
+      for (int k = 0; k < BPT; ++k) bf16x16_to_f32(w[k][0], w[k][1], v[k]);
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < BPT; ++k)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) m = fmaxf(m, __builtin_fabsf(v[k][x]));
+      const float amax = wave_max(m);
+      quantize_row_store<BPT>(v, NB, lane, 64, amax, s_q + i * q_stride(K), s_s + i * s_stride(K),
+                              s_rgs + i);
+    }
+    // this wave's LDS writes have landed (its weight loads stay in flight)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("" ::: "memory");
+    // lanes past the group's rows read its first row: their B columns feed no term
+    const int rl = r0 + (rr < G ? rr : 0);
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    nvfp4_stream_mfma<1, D, S, MOE_W_CPOL, D>(wr, K, sstride, s_q, s_s, rl, acc, rg);
+    if (rr < G) {
+      const int i = r0 + rr;
+      const float cf = ow * gdown * s_rgs[i];
+      f32x4 v = acc[0];
+      v[0] = v[0] * cf;
+      v[1] = v[1] * cf;
+      v[2] = v[2] * cf;
+      v[3] = v[3] * cf;
+      s_term[i][kq] = v;
+    }
+  }
+  if (threadIdx.x < R) s_rows[threadIdx.x] = tr;
+  if (threadIdx.x <= min(ts.T, kSumTokLds)) s_off[threadIdx.x] = to;
+  __syncthreads();
+  // the per-token sum of the tile's 16 columns: thread u takes token u / 4, columns
+  // 4 (u % 4) .. 4 (u % 4) + 3
+  for (int u = threadIdx.x; u < 4 * ts.T; u += 64 * WV) {
+    const int t = u >> 2, c4 = u & 3;
+    const int p0 = t < kSumTokLds ? s_off[t] : ts.tok_off[t];
+    const int p1 = t < kSumTokLds ? s_off[t + 1] : ts.tok_off[t + 1];
+    f32x4 part[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int base = p0; base < p1; base += 8) {
+      // the eight rows' indices, then their terms, each read as one batch (entries past the
+      // token's list are read in range and not added)
+      int ix[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ix[j] = s_rows[min(base + j, WV - 1)] & (WV - 1);
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = s_term[ix[j]][c4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (base + j < p1) {
+          part[j][0] += v[j][0];
+          part[j][1] += v[j][1];
+          part[j][2] += v[j][2];
+          part[j][3] += v[j][3];
+        }
+      }
+    }
+    f32x4 sum = part[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      sum[0] += part[j][0];
+      sum[1] += part[j][1];
+      sum[2] += part[j][2];
+      sum[3] += part[j][3];
+    }
+    u32x2 ov;
+    ov[0] = f32_to_bf16_rne(sum[0]) | (f32_to_bf16_rne(sum[1]) << 16);
+    ov[1] = f32_to_bf16_rne(sum[2]) | (f32_to_bf16_rne(sum[3]) << 16);
+    *(u32x2*)(ts.out + (size_t)t * p.N + 16 * tile + 4 * c4) = ov;
+  }
+}
+
 // ------------------------------------------------------------------------- GEMV path
 template <int NS, int D, int S>
 __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
@@ -1471,6 +1679,45 @@ hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expe
     case 4: return go(k_gemm_quantizing<4, 4, 2>);
     case 2: return go(k_gemm_quantizing<2, 2, 2>);
     default: return go(k_gemm_quantizing<1, 1, 2>);
+  }
+}
+
+// (K above 2048 with 16 waves would spill: four blocks of h per lane and the ring)
+bool grouped_gemm_quantizing_sum_fits(int R, int K) {
+  return R >= 1 && R <= 16 && K <= (R <= 8 ? 4096 : 2048) &&
+         (K <= 1024 || scale_group(K / 128) == 8);
+}
+
+hipError_t launch_grouped_gemm_quantizing_sum(const uint16_t* h, int E, int R, const uint8_t* w2,
+                                              int N, int K, const float* row_w,
+                                              const float* g_down, const int4* items,
+                                              const int32_t* tok_off, const int32_t* tok_rows,
+                                              int T, uint16_t* out, hipStream_t s) {
+  if (!grouped_gemm_quantizing_sum_fits(R, K) || N % 16 != 0 || !items) return hipErrorInvalidValue;
+  GemmArgs a{nullptr, nullptr, nullptr, R, nullptr, E, w2, N, K, nullptr, 1, 0x7FFFFFFF};
+  a.c_w = row_w;
+  a.c_g = g_down;
+  a.items = items;
+  const TokenSumArgs ts{tok_off, tok_rows, T, out};
+  const int WV = R <= 8 ? 8 : 16;
+  const size_t lds = (size_t)WV * (q_stride(K) + s_stride(K)) + 256;
+  auto go = [&](auto kern) {
+    if (lds > 65536) {
+      const hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(kern, dim3(N / 16), dim3(64 * WV), lds, s, a, h, ts);
+    return hipGetLastError();
+  };
+  // (one token: an 8-chunk weight ring; two: a 4-chunk ring, as in the three-launch path)
+  if (K > 2048) return go(k_gemm_quantizing_sum<8, 8, 8, 4>);
+  if (K > 1024) return WV == 8 ? go(k_gemm_quantizing_sum<8, 8, 8, 2>) : go(k_gemm_quantizing_sum<16, 4, 8, 2>);
+  switch (scale_group(K / 128)) {
+    case 8: return WV == 8 ? go(k_gemm_quantizing_sum<8, 8, 8, 1>) : go(k_gemm_quantizing_sum<16, 4, 8, 1>);
+    case 4: return WV == 8 ? go(k_gemm_quantizing_sum<8, 4, 4, 1>) : go(k_gemm_quantizing_sum<16, 4, 4, 1>);
+    case 2: return WV == 8 ? go(k_gemm_quantizing_sum<8, 2, 2, 1>) : go(k_gemm_quantizing_sum<16, 2, 2, 1>);
+    default: return WV == 8 ? go(k_gemm_quantizing_sum<8, 1, 1, 1>) : go(k_gemm_quantizing_sum<16, 1, 1, 1>);
   }
 }
 

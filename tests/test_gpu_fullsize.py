@@ -128,11 +128,12 @@ def test_grid_instances_agree_bitwise_at_k4096(lib, full_weights, w13_ragged570)
     assert np.array_equal(small.view(np.uint32), big[rows].view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["decode1", "decode4", "decode8", "ragged570", "ragged2303",
-                                  "zipf512"])
+@pytest.mark.parametrize("name", ["decode1", "decode2", "decode4", "decode8", "ragged570",
+                                  "ragged2303", "zipf512"])
 def test_full_size_layer_equals_separate_calls(lib, full_weights, name):
     """moe_layer_forward at full size equals the separate entry points bit for bit: the
-    decode-sized launches (1 and 32 assignments: grouping and quantization inside the GEMMs),
+    decode-sized launches (8 and 16 assignments: two launches, the w2 launch summing the
+    tokens; 32: grouping and quantization inside the GEMMs, then the per-token sum),
     the five-launch path with small-grid (64 rows) and large-grid GEMMs, and the Zipf batch's
     multi-pass groups."""
     from nvfp4_block_scaled_gather_amd import binding as B

@@ -157,6 +157,42 @@ def test_single_source_row_layer_equals_separate_calls(lib, R, hot):
     assert np.array_equal(got, composed_layer(B, dl, 0, 0))
 
 
+@pytest.mark.parametrize("R,T,I,hot,bad", [(8, 3, 1024, 3, False), (8, 100, 4096, 0, True),
+                                            (12, 80, 256, 5, True), (16, 1, 2048, 0, False),
+                                            (16, 4, 512, 16, False), (9, 9, 2048, 0, False)])
+def test_w2_and_token_sum_launch_equals_separate_calls(lib, R, T, I, hot, bad):
+    """Up to 16 assignments the w2 launch also sums each token's terms (the layer is two
+    launches): bit-identical to the separate entry points at 8 and 16 waves per workgroup,
+    K = 256 to 4096, a group of 3, 5 or 16 rows, one token of 16 rows (the per-token sum's
+    eight partials of two rows each), more than 64 tokens (token offsets past the ones the
+    launch caches), tokens without rows and dropped assignments."""
+    from nvfp4_block_scaled_gather_amd import binding as B
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("w2 + token-sum launch vs separate calls", R, T, I, hot, bad)
+    base = W.make_workload("ragged2303", E=24, H=512, I=I)
+    rng = np.random.default_rng(1000 * R + T)
+    a_expert = rng.choice(base.E, R, replace=False).astype(np.int32)
+    a_expert[:hot] = 3
+    a_src = rng.integers(0, base.S, R).astype(np.int32)
+    a_dst = rng.integers(0, T, R).astype(np.int32)
+    if T > 64:
+        a_dst[:4] = [0, 64, 65, T - 1]
+    if bad:
+        a_expert[R - 1] = base.E  # expert id out of range
+        a_dst[R - 2] = T          # output row out of range
+    a_w = rng.uniform(0.05, 1.0, R).astype(np.float32)
+    wl = W.Workload(**{**base.__dict__, "T": T, "a_expert": a_expert, "a_src": a_src,
+                       "a_dst": a_dst, "a_w": a_w})
+    dl = L.DeviceLayer(wl, flags=0, gemv_max_rows=0)
+    got = host(dl.forward())
+    sync()
+    err = dl.device_error()
+    assert err == (B.MOE_ERR_EXPERT | B.MOE_ERR_DST if bad else 0), err
+    assert np.array_equal(got, composed_layer(B, dl, 0, 0))
+    assert np.count_nonzero(got) > 0
+
+
 @pytest.mark.parametrize("flags", [1, 2])
 def test_layer_batch_parity_and_determinism(lib, flags):
     """[GG] "Proof" / batch parity: a token's output is the same
@@ -333,7 +369,8 @@ def test_graph_replay_matches_eager(lib):
     from nvfp4_block_scaled_gather_amd import layer as L
     from nvfp4_block_scaled_gather_amd import workloads as W
     for name, dims in (("tiny", {}), ("ragged570", dict(E=32, H=512, I=256)),
-                       ("zipf512", dict(E=48, H=256, I=256))):
+                       ("zipf512", dict(E=48, H=256, I=256)),
+                       ("decode2", dict(E=32, H=512, I=1024))):
         say("graph", name, dims)
         wl = W.make_workload(name, **dims)
         dl = L.DeviceLayer(wl)

@@ -55,7 +55,7 @@ def test_noalloc_equals_workspace_entry_point_small_shapes(lib):
 
 def test_noalloc_equals_workspace_entry_point_full_size(lib, full_weights):
     """ragged2303 (288 experts, H=4096, I=2048: 55 MB of scratch, the largest headline
-    batch) and then single-token decode (the three-launch path) on the resident experts."""
+    batch) and then single-token decode (the two-launch path) on the resident experts."""
     from nvfp4_block_scaled_gather_amd import binding as B
     from nvfp4_block_scaled_gather_amd import layer as L
     from nvfp4_block_scaled_gather_amd import workloads as W

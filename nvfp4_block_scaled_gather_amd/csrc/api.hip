@@ -486,6 +486,13 @@ int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
                                                  (const uint8_t*)L->w13_packed, I, H, L->g_gate,
                                                  L->g_up, w.h16, stream, true, w.items);
     if (e != hipSuccess) return hip_status(e, "layer: W4A16 grouping w13 GEMM + SwiGLU launch");
+    if (moe::grouped_gemm_w4a16_sum_fits(R, I)) {
+      // at most 16 rows: the w2 launch also sums each token's terms (two launches in all)
+      e = moe::launch_grouped_gemm_w4a16_sum(w.h16, E, R, (const uint8_t*)L->w2_packed, H, I,
+                                             w.row_w, L->g_down, w.items, w.tok_off, w.tok_rows,
+                                             T, out, stream);
+      return hip_status(e, "layer: W4A16 w2 GEMM + per-token sum launch");
+    }
   } else {
     e = moe::launch_group(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
                           w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, stream, w.items);

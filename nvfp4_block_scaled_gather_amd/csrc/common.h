@@ -457,6 +457,14 @@ hipError_t launch_grouped_gemm_quantizing(const uint16_t* h, const int32_t* expe
 // same bits; items: the work list launch_grouped_gemm_swiglu_grouping wrote (required).
 // grouped_gemm_quantizing_sum_fits: whether the launch takes R rows at this K.
 bool grouped_gemm_quantizing_sum_fits(int R, int K);
+// The same for the W4A16 layer: the W4A16 w2 GEMM over bf16 rows of h [R, K] and the
+// per-token sum in one launch, the bits of launch_grouped_gemm_w4a16 + launch_token_sum.
+bool grouped_gemm_w4a16_sum_fits(int R, int K);
+hipError_t launch_grouped_gemm_w4a16_sum(const uint16_t* h, int E, int R, const uint8_t* w2,
+                                         int N, int K, const float* row_w, const float* g_down,
+                                         const int4* items, const int32_t* tok_off,
+                                         const int32_t* tok_rows, int T, uint16_t* out,
+                                         hipStream_t s);
 hipError_t launch_grouped_gemm_quantizing_sum(const uint16_t* h, int E, int R, const uint8_t* w2,
                                               int N, int K, const float* row_w,
                                               const float* g_down, const int4* items,

@@ -531,6 +531,44 @@ __device__ __forceinline__ void nvfp4_stream_mfma(__amdgpu_buffer_rsrc_t wr, int
   }, rg);
 }
 
+// The W4A16 MFMA loop of a pass, for kernels whose waves run passes of their own (the
+// decode-sized W4A16 w2 launch that also sums the tokens): streams the NS weight tiles of wr
+// against staged bf16 activation row rl (K columns, staging area s_b), with the instructions
+// of mfma_pass's W4A16 loop (kept inline there, as its NVFP4 loop is).
+template <int NS, int D, int S, int WPOL, int PRIMED>
+__device__ __forceinline__ void bf16_stream_mfma(__amdgpu_buffer_rsrc_t wr, int K, int sstride,
+                                                 const uint8_t* s_b, int rl, f32x4 (&acc)[NS],
+                                                 Ring<NS, D>& rg) {
+  const int lane = threadIdx.x & 63;
+  const int kq = lane >> 4, NC = K / 128;
+  const uint8_t* ab_l = s_b + rl * b_stride(K) + 64 * kq;
+  u32x4 b_next[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) b_next[q] = *(const u32x4*)(ab_l + 16 * q);
+  stream_weights_c<NS, D, S, WPOL, PRIMED>(wr, NC, sstride, 16 * lane, S * 1024 + 2 * S * lane,
+                           [&](int c, int j, const u32x4 (&wn)[NS], const u32x4 (&sg)[NS]) {
+    u32x4 bq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bq[q] = b_next[q];
+      b_next[q] = *(const u32x4*)(ab_l + 256 * (c + 1) + 16 * q);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // issue the reads before this chunk's work
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const f16x2 hs = __builtin_bit_cast(
+          f16x2, scale_pair_pos(sg[s][j >> 1], (j & 1) ? 0x0c030c02u : 0x0c010c00u));
+      const float f0 = (float)hs[0], f1 = (float)hs[1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8 aop = dequant8_bf16(wn[s][q], q >= 2 ? f1 : f0);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bq[q]),
+                                                         acc[s], 0, 0, 0);
+      }
+    }
+  }, rg);
+}
+
 // One pass: stage the pass's rows, then stream NS weight tiles (wt: first tile, uniform)
 // against them.  Every wave of the workgroup calls this together (it synchronizes); a
 // wave with no tile in this item (nsv <= 0) loads nothing (empty buffer range) and stores
@@ -1293,6 +1331,120 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_quantizing_sum(GemmArgs p,
   }
 }
 
+// The W4A16 counterpart of k_gemm_quantizing_sum: a batch of at most WV expert-rows, the
+// w2 GEMM over bf16 rows of h (each wave copies its group's rows into the staging area as
+// they are: bf16 activations carry no row global) and the per-token sum in one launch; the
+// terms are the W4A16 scatter-ready products acc * (row_w[i] * g_down[e]).
+template <int WV, int D, int S>
+__global__ __launch_bounds__(64 * WV) void k_gemm_w4a16_sum(GemmArgs p,
+                                                            const uint16_t* __restrict__ h,
+                                                            TokenSumArgs ts) {
+  static_assert(WV == 8 || WV == 16, "a power of two of at most 16 waves");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ f32x4 s_term[WV][4];   // scatter terms: [grouped row][4 columns x 4]
+  __shared__ int s_rows[WV];        // the token lists
+  __shared__ int s_off[kSumTokLds + 1];
+  const int K = p.K, R = p.a_rows;
+  uint8_t* s_b = smem;  // [WV rows][b_stride(K)], then 256 bytes of slack
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tile = blockIdx.x;
+  const int tr = threadIdx.x < R ? ts.tok_rows[threadIdx.x] : 0;
+  const int to = threadIdx.x <= min(ts.T, kSumTokLds) ? ts.tok_off[threadIdx.x] : 0;
+  int4 it = int4{0, 0, 0, 0};
+  if (wave < R && wave < p.E) it = p.items[1 + wave];
+  const int ng = __builtin_amdgcn_readfirstlane(p.items[0].x);
+  const bool has = wave < ng;  // uniform
+  const int e = has ? __builtin_amdgcn_readfirstlane(it.x) : 0;
+  const int r0 = has ? __builtin_amdgcn_readfirstlane(it.y) : 0;
+  const int G = has ? __builtin_amdgcn_readfirstlane(it.z) : 0;
+  const size_t expert_bytes = (size_t)p.N * K / 16 * 9;
+  const uint8_t* wt = p.w + (size_t)e * expert_bytes + (size_t)tile * 9 * K;
+  int sstride;
+  const __amdgpu_buffer_rsrc_t wr = pass_weights<false>(p, wt, has ? 1 : 0, sstride);
+  Ring<1, D> rg;
+  float ow = 0.f, gdown = 0.f;
+  const int kq = lane >> 4, rr = lane & 15;
+  if (has) {
+    // the group's rows of h into the staging area: the first row's loads go out before the
+    // weight loads (loads complete in order), the rest after
+    const int rb = 2 * K;  // bytes of a row (at most 8 KiB: 8 pieces of 16 bytes per lane)
+    u32x4 first[8];
+    const uint8_t* src0 = (const uint8_t*)(h + (size_t)r0 * K);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (16 * lane + 1024 * k < rb) first[k] = *(const u32x4*)(src0 + 16 * lane + 1024 * k);
+    ring_prime<1, D, S, MOE_W_CPOL>(rg, wr, sstride, 16 * lane, S * 1024 + 2 * S * lane);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (16 * lane + 1024 * k < rb)
+        *(u32x4*)(s_b + r0 * b_stride(K) + 16 * lane + 1024 * k) = first[k];
+    for (int r = 1; r < G; ++r) {
+      const uint8_t* src = (const uint8_t*)(h + (size_t)(r0 + r) * K);
+      uint8_t* dst = s_b + (r0 + r) * b_stride(K);
+      for (int o = 16 * lane; o < rb; o += 1024) *(u32x4*)(dst + o) = *(const u32x4*)(src + o);
+    }
+    gdown = p.c_g[e];
+    if (rr < G) ow = p.c_w[r0 + rr];
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's LDS writes have landed
+    asm volatile("" ::: "memory");
+    // lanes past the group's rows read its first row: their B columns feed no term
+    const int rl = r0 + (rr < G ? rr : 0);
+    f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+    bf16_stream_mfma<1, D, S, MOE_W_CPOL, D>(wr, K, sstride, s_b, rl, acc, rg);
+    if (rr < G) {
+      const int i = r0 + rr;
+      const float cf = ow * gdown;
+      f32x4 v = acc[0];
+      v[0] = v[0] * cf;
+      v[1] = v[1] * cf;
+      v[2] = v[2] * cf;
+      v[3] = v[3] * cf;
+      s_term[i][kq] = v;
+    }
+  }
+  if (threadIdx.x < R) s_rows[threadIdx.x] = tr;
+  if (threadIdx.x <= min(ts.T, kSumTokLds)) s_off[threadIdx.x] = to;
+  __syncthreads();
+  for (int u = threadIdx.x; u < 4 * ts.T; u += 64 * WV) {
+    const int t = u >> 2, c4 = u & 3;
+    const int p0 = t < kSumTokLds ? s_off[t] : ts.tok_off[t];
+    const int p1 = t < kSumTokLds ? s_off[t + 1] : ts.tok_off[t + 1];
+    f32x4 part[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int base = p0; base < p1; base += 8) {
+      int ix[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ix[j] = s_rows[min(base + j, WV - 1)] & (WV - 1);
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = s_term[ix[j]][c4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (base + j < p1) {
+          part[j][0] += v[j][0];
+          part[j][1] += v[j][1];
+          part[j][2] += v[j][2];
+          part[j][3] += v[j][3];
+        }
+      }
+    }
+    f32x4 sum = part[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      sum[0] += part[j][0];
+      sum[1] += part[j][1];
+      sum[2] += part[j][2];
+      sum[3] += part[j][3];
+    }
+    u32x2 ov;
+    ov[0] = f32_to_bf16_rne(sum[0]) | (f32_to_bf16_rne(sum[1]) << 16);
+    ov[1] = f32_to_bf16_rne(sum[2]) | (f32_to_bf16_rne(sum[3]) << 16);
+    *(u32x2*)(ts.out + (size_t)t * p.N + 16 * tile + 4 * c4) = ov;
+  }
+}
+
 // ------------------------------------------------------------------------- GEMV path
 template <int NS, int D, int S>
 __device__ __forceinline__ void gemv_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
@@ -1718,6 +1870,41 @@ hipError_t launch_grouped_gemm_quantizing_sum(const uint16_t* h, int E, int R, c
     case 4: return WV == 8 ? go(k_gemm_quantizing_sum<8, 4, 4, 1>) : go(k_gemm_quantizing_sum<16, 4, 4, 1>);
     case 2: return WV == 8 ? go(k_gemm_quantizing_sum<8, 2, 2, 1>) : go(k_gemm_quantizing_sum<16, 2, 2, 1>);
     default: return WV == 8 ? go(k_gemm_quantizing_sum<8, 1, 1, 1>) : go(k_gemm_quantizing_sum<16, 1, 1, 1>);
+  }
+}
+
+// (the bf16 rows of 16 waves' groups fill 66 KiB of LDS at K = 2048)
+bool grouped_gemm_w4a16_sum_fits(int R, int K) {
+  return R >= 1 && R <= 16 && K <= (R <= 8 ? 4096 : 2048);
+}
+
+hipError_t launch_grouped_gemm_w4a16_sum(const uint16_t* h, int E, int R, const uint8_t* w2,
+                                         int N, int K, const float* row_w, const float* g_down,
+                                         const int4* items, const int32_t* tok_off,
+                                         const int32_t* tok_rows, int T, uint16_t* out,
+                                         hipStream_t s) {
+  if (!grouped_gemm_w4a16_sum_fits(R, K) || N % 16 != 0 || !items) return hipErrorInvalidValue;
+  GemmArgs a{nullptr, nullptr, nullptr, R, nullptr, E, w2, N, K, nullptr, 1, 0x7FFFFFFF};
+  a.c_w = row_w;
+  a.c_g = g_down;
+  a.items = items;
+  const TokenSumArgs ts{tok_off, tok_rows, T, out};
+  const int WV = R <= 8 ? 8 : 16;
+  const size_t lds = (size_t)WV * b_stride(K) + 256;
+  auto go = [&](auto kern) {
+    if (lds > 65536) {
+      const hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(kern, dim3(N / 16), dim3(64 * WV), lds, s, a, h, ts);
+    return hipGetLastError();
+  };
+  switch (scale_group(K / 128)) {
+    case 8: return WV == 8 ? go(k_gemm_w4a16_sum<8, 8, 8>) : go(k_gemm_w4a16_sum<16, 4, 8>);
+    case 4: return WV == 8 ? go(k_gemm_w4a16_sum<8, 4, 4>) : go(k_gemm_w4a16_sum<16, 4, 4>);
+    case 2: return WV == 8 ? go(k_gemm_w4a16_sum<8, 2, 2>) : go(k_gemm_w4a16_sum<16, 2, 2>);
+    default: return WV == 8 ? go(k_gemm_w4a16_sum<8, 1, 1>) : go(k_gemm_w4a16_sum<16, 1, 1>);
   }
 }
 

@@ -341,7 +341,7 @@ def test_full_size_layer_sampled_tokens(lib, full_weights, name):
 
 
 # ------------------------------------------------------------------------------ HIP graph
-@pytest.mark.parametrize("name", ["decode8", "ragged570", "ragged2303", "zipf512"])
+@pytest.mark.parametrize("name", ["decode1", "decode8", "ragged570", "ragged2303", "zipf512"])
 def test_full_size_w4a16_sampled_tokens(lib, full_weights, name):
     """moe_layer_forward_w4a16 at full size on the resident expert set; the W4A16 oracle
     recomputes every row of a few tokens."""

@@ -239,3 +239,40 @@ def test_w4a16_layer_eight_row_passes(lib):
         alone = host(d1.forward()).view(np.uint16)
         sync()
         assert np.array_equal(alone[t], full[t]), t
+
+
+@pytest.mark.parametrize("R,T,H,I,hot", [(1, 1, 512, 256, 0), (8, 3, 512, 1024, 3),
+                                         (12, 5, 1024, 2048, 5), (16, 1, 512, 512, 0),
+                                         (16, 4, 1024, 256, 16), (8, 2, 512, 4096, 0)])
+def test_w4a16_decode_layer_equals_the_batch_path(lib, R, T, H, I, hot):
+    """Up to 16 assignments the W4A16 layer is two launches (the w2 launch also sums the
+    tokens, at 8 or 16 waves per workgroup): every token's output equals the same token's
+    output in a batch of more than 32 assignments (the general path: the w2 GEMM and the
+    per-token sum as launches of their own) bit for bit, with a group of 3, 5 or 16 rows and
+    one token of 16 rows."""
+    from nvfp4_block_scaled_gather_amd import layer as L
+    from nvfp4_block_scaled_gather_amd import workloads as W
+    say("w4a16 decode layer vs batch path", R, T, H, I, hot)
+    base = W.make_workload("ragged2303", E=24, H=H, I=I)
+    rng = np.random.default_rng(1000 * R + T + I)
+    a_expert = rng.choice(base.E, R, replace=False).astype(np.int32)
+    a_expert[:hot] = 3
+    a_src = rng.integers(0, base.S, R).astype(np.int32)
+    a_dst = rng.integers(0, T, R).astype(np.int32)
+    a_w = rng.uniform(0.05, 1.0, R).astype(np.float32)
+    small = W.Workload(**{**base.__dict__, "T": T, "a_expert": a_expert, "a_src": a_src,
+                          "a_dst": a_dst, "a_w": a_w})
+    n = 40  # more assignments, to other tokens: the batch takes the general path
+    big = W.Workload(**{**base.__dict__, "T": T + 10,
+                        "a_expert": np.concatenate([a_expert, rng.integers(0, base.E, n)]).astype(np.int32),
+                        "a_src": np.concatenate([a_src, rng.integers(0, base.S, n)]).astype(np.int32),
+                        "a_dst": np.concatenate([a_dst, rng.integers(T, T + 10, n)]).astype(np.int32),
+                        "a_w": np.concatenate([a_w, rng.uniform(0.05, 1.0, n)]).astype(np.float32)})
+    d1 = L.DeviceLayer(small, arithmetic="w4a16")
+    d2 = L.DeviceLayer(big, weights=(d1.w13, d1.w2), arithmetic="w4a16")
+    got = host(d1.forward()).copy()
+    want = host(d2.forward()).copy()
+    sync()
+    assert d1.device_error() == 0 and d2.device_error() == 0
+    assert np.count_nonzero(got) > 0
+    assert np.array_equal(got, want[:T])

@@ -159,7 +159,8 @@ def test_single_source_row_layer_equals_separate_calls(lib, R, hot):
 
 @pytest.mark.parametrize("R,T,I,hot,bad", [(8, 3, 1024, 3, False), (8, 100, 4096, 0, True),
                                             (12, 80, 256, 5, True), (16, 1, 2048, 0, False),
-                                            (16, 4, 512, 16, False), (9, 9, 2048, 0, False)])
+                                            (16, 4, 512, 16, False), (9, 9, 2048, 0, False),
+                                            (8, 5, 2048, 2, True), (1, 1, 2048, 0, False)])
 def test_w2_and_token_sum_launch_equals_separate_calls(lib, R, T, I, hot, bad):
     """Up to 16 assignments the w2 launch also sums each token's terms (the layer is two
     launches): bit-identical to the separate entry points at 8 and 16 waves per workgroup,

@@ -1406,6 +1406,9 @@ __global__ __launch_bounds__(64 * WV) void k_gemm_w4a16_sum(GemmArgs p,
   if (threadIdx.x < R) s_rows[threadIdx.x] = tr;
   if (threadIdx.x <= min(ts.T, kSumTokLds)) s_off[threadIdx.x] = to;
   __syncthreads();
+  // the per-token sum, as in k_gemm_quantizing_sum.  The two copies stay inline: one shared
+  // device function, force-inlined, still changed both kernels' code (the W4A16 one with
+  // eight waves grew by a third, in register moves).
   for (int u = threadIdx.x; u < 4 * ts.T; u += 64 * WV) {
     const int t = u >> 2, c4 = u & 3;
     const int p0 = t < kSumTokLds ? s_off[t] : ts.tok_off[t];

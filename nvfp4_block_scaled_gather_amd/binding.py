@@ -23,6 +23,7 @@ MOE_PATH_FORCE_MFMA = 2
 MOE_ERR_EXPERT = 1
 MOE_ERR_SRC = 2
 MOE_ERR_DST = 4
+MOE_ERR_SYNC = 8
 
 # Default largest group on the GEMV path under MOE_PATH_AUTO.  Measured on MI355X, the MFMA
 # path streams the weights faster than the GEMV path for every group size, one row included,

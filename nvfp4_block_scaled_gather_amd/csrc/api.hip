@@ -262,6 +262,8 @@ struct LayerWs {
   float* hgs;
   uint16_t* h16;  // W4A16: h [R, I] bf16 (the w2 GEMM's input while acc takes its output)
   int4* items;    // the grouped GEMMs' work list, E + 1 entries
+  int* sync;      // the one-launch GEMM pair's flags (grouped_gemm_layer_sync_ints)
+  int nsync;
   size_t bytes;
 };
 
@@ -292,6 +294,8 @@ LayerWs carve(const moe_layer_desc* L, int S, int R, int T, uint8_t* base) {
   w.hgs = (float*)take(4 * r);
   w.h16 = (uint16_t*)take(2 * r * L->I);
   w.items = (int4*)take(sizeof(int4) * ((size_t)L->E + 1));
+  w.nsync = moe::grouped_gemm_layer_sync_ints(L->E, R, L->H, L->I);
+  w.sync = (int*)take(4 * (size_t)w.nsync);
   w.bytes = o;
   return w;
 }
@@ -380,10 +384,25 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
   // grouped row i from source row row_src[i], so no gathered copy of x is made
   // (the work list is written and used only when every group is on the MFMA path)
   int4* items = all_mfma && R > 32 ? w.items : nullptr;
+  const bool one_launch = all_mfma && R > 32 && moe::grouped_gemm_layer_fits(E, R, H, I);
   e = moe::launch_group_quantize(a_expert, a_src, a_dst, a_w, R, E, S, T, w.offsets, w.row_src,
                                  w.row_dst, w.row_w, w.tok_off, w.tok_rows, w.err, x, H, w.xq,
-                                 w.xs, w.xgs, items, stream);
+                                 w.xs, w.xgs, items, stream, one_launch ? w.sync : nullptr,
+                                 one_launch ? w.nsync : 0);
   if (e != hipSuccess) return hip_status(e, "layer: group+quantize launch");
+  if (one_launch) {
+    // a batch that fills the large grid: w13 + SwiGLU, the quantization of h and w2 in one
+    // launch (h in its own buffer, since the w2 items write their terms into acc while
+    // other groups' rows of h are still read), then the per-token sum; the same bits
+    e = moe::launch_grouped_gemm_layer(w.xq, w.xs, w.row_src, S, w.offsets, E, R,
+                                       (const uint8_t*)L->w13_packed,
+                                       (const uint8_t*)L->w2_packed, I, H, L->g_gate, L->g_up,
+                                       w.xgs, w.h16, w.hq, w.hs, w.hgs, w.row_w, L->g_down, w.acc,
+                                       w.items, w.sync, w.err, stream);
+    if (e != hipSuccess) return hip_status(e, "layer: fused GEMM launch");
+    e = moe::launch_token_sum(w.acc, R, H, w.tok_off, w.tok_rows, T, out, stream);
+    return hip_status(e, "layer: scatter launch");
+  }
   if (all_mfma) {
     // SwiGLU in the w13 GEMM's epilogue (h in bf16 instead of the fp32 gate|up products),
     // then the NVFP4 quantization of h; the same bits as the unfused sequence below

@@ -207,13 +207,12 @@ __device__ __forceinline__ float row_amax_threads(const float (&v)[BPT][16], int
   return amax;
 }
 
-// Step 2: codes, scale bytes and the row global (no barrier; call only for real rows).
-template <int BPT>
-__device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], int NB, int t,
-                                                   int nthreads, float amax,
-                                                   uint8_t* __restrict__ q,
-                                                   uint8_t* __restrict__ sc,
-                                                   float* __restrict__ gs_out) {
+// Step 2: codes, scale bytes and the row global (no barrier; call only for real rows),
+// handed to `st`: st.codes(b, {lo, hi}) for block b's 16 codes (8 bytes, element order),
+// st.scale(b, byte) for its scale byte, st.global(gs) (by thread 0).
+template <int BPT, class Store>
+__device__ __forceinline__ void quantize_row_emit(const float (&v)[BPT][16], int NB, int t,
+                                                  int nthreads, float amax, Store& st) {
 #pragma clang fp contract(off)
   const float gs = amax > 0.0f ? amax / 2688.0f : 1.0f;
   const float tg = 6.0f * gs;
@@ -255,11 +254,31 @@ __device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], in
       lo = e2m1x8_encode(qv);
       hi = e2m1x8_encode(qv + 8);
     }
-    u32x2 pk = {lo, hi};
-    *(u32x2*)(q + 8 * (size_t)b) = pk;
-    sc[b] = (uint8_t)sb;
+    st.codes(b, u32x2{lo, hi});
+    st.scale(b, sb);
   }
-  if (t == 0) *gs_out = gs;
+  if (t == 0) st.global(gs);
+}
+
+// Plain stores of a quantized row: codes at q (NB x 8 bytes), scale bytes at sc, the
+// global at *gs_out.
+struct RowStorePlain {
+  uint8_t* __restrict__ q;
+  uint8_t* __restrict__ sc;
+  float* __restrict__ gs_out;
+  __device__ __forceinline__ void codes(int b, const u32x2& v) { *(u32x2*)(q + 8 * (size_t)b) = v; }
+  __device__ __forceinline__ void scale(int b, uint32_t sb) { sc[b] = (uint8_t)sb; }
+  __device__ __forceinline__ void global(float gs) { *gs_out = gs; }
+};
+
+template <int BPT>
+__device__ __forceinline__ void quantize_row_store(const float (&v)[BPT][16], int NB, int t,
+                                                   int nthreads, float amax,
+                                                   uint8_t* __restrict__ q,
+                                                   uint8_t* __restrict__ sc,
+                                                   float* __restrict__ gs_out) {
+  RowStorePlain st{q, sc, gs_out};
+  quantize_row_emit<BPT>(v, NB, t, nthreads, amax, st);
 }
 
 // The grouped GEMM's work list, written by the grouping: the non-empty groups in the order
@@ -417,6 +436,22 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
                                int gemv_max_rows, hipStream_t s, const float* c_w = nullptr,
                                const float* c_g = nullptr, const float* c_gs = nullptr,
                                const int4* items = nullptr);
+// The layer's w13 GEMM with the SwiGLU epilogue, the NVFP4 quantization of h and the w2
+// GEMM with the scatter-ready epilogue in one launch (MFMA path for every group, the
+// grouping's work list `items`): h [R, I] bf16, hq / hs / hgs and the terms [R, H] are the
+// bits of launch_grouped_gemm_swiglu + launch_quantize + launch_grouped_gemm.  sync:
+// grouped_gemm_layer_sync_ints(E, R, H, I) ints, zero on entry (launch_group_quantize
+// clears them); err: the device error word (MOE_ERR_SYNC is ORed in if a bounded wait gave
+// up).  Only where grouped_gemm_layer_fits(E, R, H, I).
+bool grouped_gemm_layer_fits(int E, int R, int H, int I);
+int grouped_gemm_layer_sync_ints(int E, int R, int H, int I);  // 0 where it does not fit
+hipError_t launch_grouped_gemm_layer(const uint8_t* xq, const uint8_t* xs, const int32_t* row_src,
+                                     int S, const int32_t* off, int E, int R, const uint8_t* w13,
+                                     const uint8_t* w2, int I, int H, const float* g_gate,
+                                     const float* g_up, const float* xgs, uint16_t* h,
+                                     uint8_t* hq, uint8_t* hs, float* hgs, const float* row_w,
+                                     const float* g_down, float* terms, const int4* items,
+                                     int* sync, int32_t* err, hipStream_t s);
 // The w13 GEMM with SwiGLU applied in its epilogue (MFMA path for every group): the
 // fused [2I, K] gate|up weights give h [R, I] bf16 for the grouped rows, equal bit for bit
 // to launch_grouped_gemm followed by launch_swiglu.  Rows outside every group are not
@@ -486,13 +521,14 @@ hipError_t launch_grouped_gemm_swiglu_w4a16(const uint16_t* ab, const int32_t* a
 // Grouping and NVFP4 quantization of the S source rows of x in one launch (independent
 // work: block 0 groups, the other blocks quantize four rows each).  items (E + 1 entries,
 // or nullptr): for more than 32 assignments, also the grouped GEMM's work list (see
-// kWorkListMultiRows).
+// kWorkListMultiRows).  zero[0 .. nzero) is cleared (the fused GEMM launch's counters).
 hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, const int32_t* a_dst,
                                  const float* a_w, int R, int E, int S, int T,
                                  int32_t* expert_offsets, int32_t* row_src, int32_t* row_dst,
                                  float* row_w, int32_t* tok_off, int32_t* tok_rows,
                                  int32_t* err_word, const uint16_t* x, int H, uint8_t* xq,
-                                 uint8_t* xs, float* xgs, int4* items, hipStream_t s);
+                                 uint8_t* xs, float* xgs, int4* items, hipStream_t s,
+                                 int* zero = nullptr, int nzero = 0);
 hipError_t launch_scatter(const float* y, int R, int H, const int32_t* expert_offsets, int E,
                           const float* row_w, const float* g_down, const float* row_gs,
                           const int32_t* tok_off, const int32_t* tok_rows, int T, uint16_t* out,

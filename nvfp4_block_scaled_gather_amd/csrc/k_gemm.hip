@@ -30,6 +30,8 @@
 // MFMA path with k_gemm_mfma's passes and arithmetic: k_gemm_swiglu_grouping (w13 with the
 // SwiGLU epilogue, each workgroup grouping the assignments and quantizing its group's
 // source rows itself) and k_gemm_quantizing (w2, each workgroup quantizing its rows of h).
+// k_gemm_layer runs the layer's two GEMMs and the quantization of h between them as one
+// launch for batches that fill the large grid (k_gemm_mfma's items, flags between them).
 //
 // Outputs are written as whole rows of the workgroup's block (store_out): measured on
 // MI355X, write-back stores that are later evicted from L2 in the middle of the weight
@@ -231,12 +233,31 @@ __device__ __forceinline__ void store_out(const u32x4& v, __amdgpu_buffer_rsrc_t
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Cache policy SC1 of a buffer access: device scope.  A store is written through this
+// XCD's L2, and a load does not take a line that this L2 may hold from before another XCD
+// wrote it; with these, data passes between workgroups of one launch without cache
+// maintenance (the writer waits for its stores to complete before it signals).
+constexpr int kDeviceScope = 16;
+
+// Activation global of pass row r (< nrows) of rows arow0 ..: read at device scope when
+// APOL says so (the rows' globals were written earlier in the same launch).
+template <int APOL>
+__device__ __forceinline__ float pass_row_global(const float* gs, int arow0, int nrows, int r) {
+  if constexpr (APOL == 0) {
+    return gs[arow0 + r];
+  } else {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gs + arow0, nrows * 4);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * r, 0, APOL));
+  }
+}
+
 // Stage activation rows arow0 .. arow0 + nrows - 1 (through amap) into LDS with
 // buffer-to-LDS loads: wave w copies rows w, w + WAVES, ...; an NVFP4 row is K/2 nibble
 // bytes in 1 KiB pieces (16 bytes per lane) and K/16 scale bytes in 256-byte pieces (4
 // bytes per lane); a bf16 row (ABF) is 2K bytes in 1 KiB pieces.  The caller waits for the
-// loads and synchronizes before reading.
-template <bool ABF, int WAVES>
+// loads and synchronizes before reading.  APOL: the loads' cache policy (kDeviceScope for
+// rows written earlier in the same launch by other workgroups).
+template <bool ABF, int WAVES, int APOL = 0>
 __device__ __forceinline__ void stage_rows(const GemmArgs& p, int arow0, int nrows, uint8_t* s_q,
                                            uint8_t* s_s) {
   const int lane = threadIdx.x & 63;
@@ -251,7 +272,7 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, int arow0, int nro
       for (int o = 0; o < rb; o += 1024) {
         if (o + 16 * lane < rb)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_ptr_t)(db + o), 16, 16 * lane,
-                                                   src * rb + o, 0, 0);
+                                                   src * rb + o, 0, APOL);
       }
     }
   } else {
@@ -266,12 +287,12 @@ __device__ __forceinline__ void stage_rows(const GemmArgs& p, int arow0, int nro
       for (int o = 0; o < qb; o += 1024) {
         if (o + 16 * lane < qb)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(dq + o), 16, 16 * lane,
-                                                   src * qb + o, 0, 0);
+                                                   src * qb + o, 0, APOL);
       }
       for (int o = 0; o < sb; o += 256) {
         if (o + 4 * lane < sb)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(ds + o), 4, 4 * lane,
-                                                   src * sb + o, 0, 0);
+                                                   src * sb + o, 0, APOL);
       }
     }
   }
@@ -586,7 +607,7 @@ __device__ __forceinline__ void bf16_stream_mfma(__amdgpu_buffer_rsrc_t wr, int 
 // on pass_weights<SWI>(p, wt, nsv, .)), so that their latency overlapped the quantization.
 // With FQ the barrier below waits for LDS only, leaving weight loads in flight.
 template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, bool FQ = false,
-          int WPOL = MOE_W_CPOL, int PRIMED = 0>
+          int WPOL = MOE_W_CPOL, int PRIMED = 0, int APOL = 0>
 __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                           int nsv, int arow0, int nrows, int col0,
                                           uint8_t* s_q, uint8_t* s_s, float ggate, float gup,
@@ -609,7 +630,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
   float ow = 0.f, ogs = 1.f;
   if (!SWI && p.c_w && r < nrows) {
     ow = p.c_w[arow0 + r];
-    if (!FQ && p.c_gs) ogs = p.c_gs[arow0 + r];
+    if (!FQ && p.c_gs) ogs = pass_row_global<APOL>(p.c_gs, arow0, nrows, r);
   }
 
   if constexpr (FQ) {
@@ -621,7 +642,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   } else {
-    stage_rows<ABF, WAVES>(p, arow0, nrows, s_q, s_s);
+    stage_rows<ABF, WAVES, APOL>(p, arow0, nrows, s_q, s_s);
     __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
     __syncthreads();
   }
@@ -699,7 +720,7 @@ __device__ __forceinline__ void mfma_pass(const GemmArgs& p, const uint8_t* __re
 
 // Stage K-half hf (columns [hf K/2, (hf + 1) K/2)) of NVFP4 rows arow0 .. arow0 + nrows - 1
 // into LDS as rows of K/2 columns (row strides q_stride(K/2) and s_stride(K/2)).
-template <int WAVES>
+template <int WAVES, int APOL = 0>
 __device__ __forceinline__ void stage_rows_half(const GemmArgs& p, int arow0, int nrows, int hf,
                                                 uint8_t* s_q, uint8_t* s_s) {
   const int lane = threadIdx.x & 63;
@@ -715,12 +736,12 @@ __device__ __forceinline__ void stage_rows_half(const GemmArgs& p, int arow0, in
     for (int o = 0; o < hq; o += 1024) {
       if (o + 16 * lane < hq)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_ptr_t)(dq + o), 16, 16 * lane,
-                                                 src * qb + hf * hq + o, 0, 0);
+                                                 src * qb + hf * hq + o, 0, APOL);
     }
     for (int o = 0; o < hs; o += 256) {
       if (o + 4 * lane < hs)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(ds + o), 4, 4 * lane,
-                                                 src * sb + hf * hs + o, 0, 0);
+                                                 src * sb + hf * hs + o, 0, APOL);
     }
   }
 }
@@ -735,7 +756,7 @@ __device__ __forceinline__ void stage_rows_half(const GemmArgs& p, int arow0, in
 // half starts a scale group.  The B operands are read from LDS in the chunk that uses them
 // (no read-ahead): the two operands' registers keep the instance within 128 registers per
 // lane, four waves per SIMD.
-template <int NS, int D, int S, bool SWI, int WAVES, int WPOL>
+template <int NS, int D, int S, bool SWI, int WAVES, int WPOL, int APOL = 0>
 __device__ __forceinline__ void mfma_dpass(const GemmArgs& p, const uint8_t* __restrict__ wt,
                                            int nsv, int arow0, int nrows, int col0,
                                            uint8_t* s_q, float ggate, float gup) {
@@ -756,7 +777,7 @@ __device__ __forceinline__ void mfma_dpass(const GemmArgs& p, const uint8_t* __r
     const int rr = r + kPassRows * hr;
     if (!SWI && p.c_w && rr < nrows) {
       ow[hr] = p.c_w[arow0 + rr];
-      if (p.c_gs) ogs[hr] = p.c_gs[arow0 + rr];
+      if (p.c_gs) ogs[hr] = pass_row_global<APOL>(p.c_gs, arow0, nrows, rr);
     }
   }
   // lanes past the pass's rows read row 0: their B columns only feed rows not stored
@@ -769,7 +790,7 @@ __device__ __forceinline__ void mfma_dpass(const GemmArgs& p, const uint8_t* __r
     for (int s = 0; s < NS; ++s) acc[hr][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int hf = 0; hf < 2; ++hf) {
     if (hf) __syncthreads();  // every wave is done with the first half's rows
-    stage_rows_half<WAVES>(p, arow0, nrows, hf, s_q, s_s);
+    stage_rows_half<WAVES, APOL>(p, arow0, nrows, hf, s_q, s_s);
     __builtin_amdgcn_s_waitcnt(0);  // the staged rows have landed in LDS
     __syncthreads();
     const int hrange = range == 0 ? 0 : hf ? range - hoff : range;
@@ -806,29 +827,29 @@ __device__ __forceinline__ void mfma_dpass(const GemmArgs& p, const uint8_t* __r
                                                  gup, nullptr, ow, ogs);
 }
 
-// One workgroup per item: item it covers tiles [ii * per_item, (ii + 1) * per_item) of active
-// group it / items_per_e (ii = it % items_per_e).  The grid has one item slot per group
-// that can be non-empty, so every item has a workgroup and no workgroup has two.
-// PR: activation rows staged per pass (at most the B operand's 16 columns).  Groups of
-// more than PR rows take double passes where they can (mfma_dpass); the waves-per-SIMD
-// hint keeps the 4-chunk-ring NVFP4 instances at four waves per SIMD with the double
-// pass's registers (without it they compile to three).
-template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, int PR>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(ABF || D > 4 ? 1 : 4)))
-void k_gemm_mfma(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_grp[4];
+// Item ii (of items_per_item(p)) of group g: the tiles [ii * per_item, (ii + 1) * per_item)
+// of the group's weights against all of its rows.  PR: activation rows staged per pass (at
+// most the B operand's 16 columns).  Groups of more than PR rows take double passes where
+// they can (mfma_dpass).  APOL: cache policy of the activation loads.
+template <bool SWI, int NS, int WAVES>
+__host__ __device__ __forceinline__ int item_tiles(const GemmArgs& p) {
+  return SWI ? p.I / 16 : p.N / 16;  // SWI: a wave owns one gate tile (and its up tile)
+}
+template <bool SWI, int NS, int WAVES>
+__host__ __device__ __forceinline__ int items_per_group(const GemmArgs& p) {
+  constexpr int per_item = SWI ? WAVES : WAVES * NS;
+  return (item_tiles<SWI, NS, WAVES>(p) + per_item - 1) / per_item;
+}
+
+template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, int PR, int APOL = 0>
+__device__ __forceinline__ void run_item(const GemmArgs& p, int ii, const ItemGroup& g,
+                                         uint8_t* smem) {
   uint8_t* s_q = smem;
   uint8_t* s_s = s_q + PR * q_stride(p.K);  // NVFP4 scales (unused with ABF)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // SWI: a wave owns one gate tile (and the matching up tile)
-  const int tiles = SWI ? p.I / 16 : p.N / 16;
-  const int per_item = SWI ? WAVES : WAVES * NS;
-  const int items_per_e = (tiles + per_item - 1) / per_item;
-  const int item = blockIdx.x;
-  ItemGroup g;
-  if (!find_group<PR>(p, item / items_per_e, s_grp, g)) return;  // uniform
-  const int t0 = (item % items_per_e) * per_item + wave * (SWI ? 1 : NS);
+  const int tiles = item_tiles<SWI, NS, WAVES>(p);
+  constexpr int per_item = SWI ? WAVES : WAVES * NS;
+  const int t0 = ii * per_item + wave * (SWI ? 1 : NS);
   const int nsv = SWI ? (t0 < tiles ? 2 : 0) : min(NS, tiles - t0);
   const size_t expert_bytes = (size_t)p.N * p.K / 16 * 9;
   const size_t tile_bytes = (size_t)9 * p.K;
@@ -843,23 +864,195 @@ void k_gemm_mfma(GemmArgs p) {
       if ((p.K / 128) % (2 * S) == 0) {
         for (; g.G - b > PR; b += kDPassRows) {
           if (b) __syncthreads();  // the previous pass is done with the staged rows
-          mfma_dpass<NS, D, S, SWI, WAVES, kMultiPassWCpol>(
+          mfma_dpass<NS, D, S, SWI, WAVES, kMultiPassWCpol, APOL>(
               p, wt, nsv, g.r0 + b, min(kDPassRows, g.G - b), 16 * t0, s_q, ggate, gup);
         }
       }
     }
     for (; b < g.G; b += PR) {
       if (b) __syncthreads();  // the previous pass is done with the staged rows
-      mfma_pass<NS, D, S, SWI, ABF, WAVES, false, kMultiPassWCpol>(
+      mfma_pass<NS, D, S, SWI, ABF, WAVES, false, kMultiPassWCpol, 0, APOL>(
           p, wt, nsv, g.r0 + b, min(PR, g.G - b), 16 * t0, s_q, s_s, ggate, gup);
     }
     return;
   }
   for (int b = 0; b < g.G; b += PR) {
     if (b) __syncthreads();  // the previous pass is done with the staged rows
-    mfma_pass<NS, D, S, SWI, ABF, WAVES>(p, wt, nsv, g.r0 + b, min(PR, g.G - b), 16 * t0,
-                                         s_q, s_s, ggate, gup);
+    mfma_pass<NS, D, S, SWI, ABF, WAVES, false, MOE_W_CPOL, 0, APOL>(
+        p, wt, nsv, g.r0 + b, min(PR, g.G - b), 16 * t0, s_q, s_s, ggate, gup);
   }
+}
+
+// One workgroup per item: item it is item it % items_per_e of active group it / items_per_e.
+// The grid has one item slot per group that can be non-empty, so every item has a
+// workgroup and no workgroup has two.  The waves-per-SIMD hint keeps the 4-chunk-ring
+// NVFP4 instances at four waves per SIMD with the double pass's registers (without it they
+// compile to three).
+template <int NS, int D, int S, bool SWI, bool ABF, int WAVES, int PR>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(ABF || D > 4 ? 1 : 4)))
+void k_gemm_mfma(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_grp[4];
+  const int items_per_e = items_per_group<SWI, NS, WAVES>(p);
+  const int item = blockIdx.x;
+  ItemGroup g;
+  if (!find_group<PR>(p, item / items_per_e, s_grp, g)) return;  // uniform
+  run_item<NS, D, S, SWI, ABF, WAVES, PR>(p, item % items_per_e, g, smem);
+}
+
+// ------------------------------------------------------------------------- fused layer
+// The layer's w13 GEMM (SwiGLU epilogue), the NVFP4 quantization of h and the w2 GEMM
+// (scatter-ready epilogue) in one launch, for batches that fill the large grid.  The grid
+// is three ranges, each in the work list's order: [0, n13) the w13 items, then one
+// quantization workgroup per group, then the w2 items.  A w13 item raises its own flag once
+// its part of h is written; a group's quantization workgroup waits for the flags of the
+// group's w13 items, quantizes the group's rows of h and raises the group's flag; a w2
+// item waits for that flag.  So the w2 items fill the slots that the w13 GEMM's last round
+// leaves free, and the quantization runs in that round too, instead of as a launch of its
+// own between the two GEMMs.
+//
+// Why it cannot deadlock: workgroups are dispatched in index order (per XCD), so a waiting
+// workgroup was dispatched after every workgroup it waits for (all earlier in the grid), and
+// the w13 items wait for nothing; every wait is bounded regardless (kSyncSpinMax polls, then
+// the error bit MOE_ERR_SYNC and no further waiting).
+//
+// Visibility without cache maintenance: h, hq, hs, hgs and the flags are written with
+// device-scope stores (through the L2) and read with device-scope loads, and a writer waits
+// for its stores to complete before it raises its flag (one thread, after a barrier).
+// Plain flag stores, one word per item: measured on MI355X, one device-scope atomic add
+// per w13 item (a counter per group, the last item quantizing) made the layer 12-14%
+// slower, with or without using the returned value, while the wait for the stores costs
+// nothing measurable.  The arithmetic of every output is k_gemm_mfma's and k_quantize's, so
+// the results are the bits of the separate launches.
+struct LayerSync {
+  int n13;         // workgroups of the w13 GEMM: n13 / groups per group
+  int groups;      // group slots (min(E, R)): kQuantParts quantization workgroups each,
+                   // then the w2 GEMM's workgroups
+  int* done13;     // [n13] nonzero once w13 item slot b has written its part of h
+  int* ready;      // [kQuantParts x groups] nonzero once part j of group a is quantized
+  int32_t* err;    // device error word
+  uint8_t* hq;     // NVFP4 h: codes [R, I/2], scales [R, I/16], row globals [R]
+  uint8_t* hs;
+  float* hgs;
+};
+constexpr int kSyncSpinMax = 1 << 19;
+
+// Lane l < n of wave 0: flags[l], read at device scope (1 elsewhere).  Issued at the start
+// of a workgroup, so that its latency overlaps the work list lookup.
+__device__ __forceinline__ int load_flags(const int* flags, int n) {
+  const int lane = threadIdx.x & 63;
+  return threadIdx.x < 64 && lane < n
+             ? __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+}
+
+// Wave 0 waits until the n flags at flags[0 .. n) (n <= 64; v: load_flags's first read)
+// are all nonzero, polling with device-scope loads; gives up after kSyncSpinMax polls and
+// sets MOE_ERR_SYNC.  The workgroup meets at a barrier afterwards.
+__device__ __forceinline__ void wait_flags(int v, const int* flags, int n, int32_t* err) {
+  if (threadIdx.x < 64) {
+    bool done = __ballot(v == 0) == 0ull;
+    for (int k = 0; !done && k < kSyncSpinMax; ++k) {
+      __builtin_amdgcn_s_sleep(8);
+      done = __ballot(load_flags(flags, n) == 0) == 0ull;
+    }
+    if (!done && threadIdx.x == 0)
+      __hip_atomic_fetch_or(err, MOE_ERR_SYNC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  asm volatile("" ::: "memory");
+}
+
+// Once every store of this workgroup has completed: flag = 1 (device scope).
+__device__ __forceinline__ void raise_flag(int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct RowStoreDevice {
+  __amdgpu_buffer_rsrc_t q, sc, gs;
+  __device__ __forceinline__ void codes(int b, const u32x2& v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, q, 8 * b, 0, kDeviceScope);
+  }
+  __device__ __forceinline__ void scale(int b, uint32_t sb) {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, sc, b, 0, kDeviceScope);
+  }
+  __device__ __forceinline__ void global(float g) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g), gs, 0, 0, kDeviceScope);
+  }
+};
+
+// Part j of the quantization of a group's rows r0 .. r0 + G - 1 of h (bf16, I columns) to
+// NVFP4: the 16-row blocks j, j + kQuantParts, ... of the group, one row per wave at a time
+// (lane l: scale blocks l + 64 k, k < BPT), with k_quantize's arithmetic.
+constexpr int kQuantParts = 4;
+template <int BPT>
+__device__ __forceinline__ void quantize_h_rows(const uint16_t* h, int I, int r0, int G, int j,
+                                                const LayerSync& f) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NB = I / 16;
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(h + (size_t)r0 * I, G * I * 2);
+  for (int b0 = 16 * j; b0 < G; b0 += 16 * kQuantParts)
+  for (int row = b0 + wave; row < min(G, b0 + 16); row += kGemmWaves) {
+    float v[BPT][16];
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int blk = lane + 64 * k;
+      u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+      if (blk < NB) {
+        w0 = __builtin_amdgcn_raw_buffer_load_b128(hr, (row * I + 16 * blk) * 2, 0, kDeviceScope);
+        w1 = __builtin_amdgcn_raw_buffer_load_b128(hr, (row * I + 16 * blk) * 2 + 16, 0,
+                                                   kDeviceScope);
+      }
+      bf16x16_to_f32(w0, w1, v[k]);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, __builtin_fabsf(v[k][e]));
+    const float amax = wave_max(m);
+    const int i = r0 + row;
+    RowStoreDevice st{make_rsrc(f.hq + (size_t)i * (I / 2), I / 2),
+                      make_rsrc(f.hs + (size_t)i * NB, NB), make_rsrc(f.hgs + i, 4)};
+    quantize_row_emit<BPT>(v, NB, lane, 64, amax, st);
+  }
+}
+
+template <int D, int S, int BPT>
+__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(4)))
+void k_gemm_layer(GemmArgs p13, GemmArgs p2, LayerSync f) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_grp[4];
+  ItemGroup g;
+  const int b = blockIdx.x;
+  const int ipe13 = items_per_group<true, 2, kGemmWaves>(p13);
+  if (b < f.n13) {  // uniform: a w13 item
+    if (!find_group<kPassRows>(p13, b / ipe13, s_grp, g)) return;  // uniform
+    run_item<2, D, S, true, false, kGemmWaves, kPassRows>(p13, b % ipe13, g, smem);
+    raise_flag(f.done13 + b);
+    return;
+  }
+  if (b < f.n13 + kQuantParts * f.groups) {  // uniform: part j of group a's quantization
+    const int a = (b - f.n13) / kQuantParts, j = (b - f.n13) % kQuantParts;
+    const int v = load_flags(f.done13 + a * ipe13, ipe13);
+    if (!find_group<kPassRows>(p13, a, s_grp, g)) return;  // uniform
+    if (16 * j < g.G) {  // uniform
+      wait_flags(v, f.done13 + a * ipe13, ipe13, f.err);
+      quantize_h_rows<BPT>(p13.h, p13.I, g.r0, g.G, j, f);
+    }
+    raise_flag(f.ready + b - f.n13);
+    return;
+  }
+  // a w2 item
+  const int ipe2 = items_per_group<false, 2, kGemmWaves>(p2);
+  const int item = b - f.n13 - kQuantParts * f.groups;
+  const int* ready = f.ready + kQuantParts * (item / ipe2);
+  const int v = load_flags(ready, kQuantParts);
+  if (!find_group<kPassRows>(p2, item / ipe2, s_grp, g)) return;  // uniform
+  wait_flags(v, ready, kQuantParts, f.err);
+  run_item<2, D, S, false, false, kGemmWaves, kPassRows, kDeviceScope>(p2, item % ipe2, g, smem);
 }
 
 // ------------------------------------------------------------------------- decode w13
@@ -1662,6 +1855,65 @@ hipError_t launch_grouped_gemm(const uint8_t* aq, const uint8_t* as, const int32
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+bool grouped_gemm_layer_fits(int E, int R, int H, int I) {
+  // both GEMMs on their large-grid instances with the 8-chunk scale group, and rows of h
+  // that one wave quantizes with at most two scale blocks per lane
+  if (R < 1 || H % 1024 || I % 1024 || I > 2048) return false;
+  GemmArgs a13{};
+  a13.E = E;
+  a13.N = 2 * I;
+  a13.K = H;
+  GemmArgs a2{};
+  a2.E = E;
+  a2.N = H;
+  a2.K = I;
+  return !small_grid(a13, R) && !small_grid(a2, R);
+}
+
+int grouped_gemm_layer_sync_ints(int E, int R, int H, int I) {
+  if (!grouped_gemm_layer_fits(E, R, H, I)) return 0;
+  GemmArgs a13{};
+  a13.E = E;
+  a13.N = 2 * I;
+  a13.K = H;
+  a13.I = I;
+  const int n13 = gemm_grid(2 * kGemmWaves, a13, R);
+  return n13 + kQuantParts * (n13 / items_per_group<true, 2, kGemmWaves>(a13));
+}
+
+hipError_t launch_grouped_gemm_layer(const uint8_t* xq, const uint8_t* xs, const int32_t* row_src,
+                                     int S, const int32_t* off, int E, int R, const uint8_t* w13,
+                                     const uint8_t* w2, int I, int H, const float* g_gate,
+                                     const float* g_up, const float* xgs, uint16_t* h,
+                                     uint8_t* hq, uint8_t* hs, float* hgs, const float* row_w,
+                                     const float* g_down, float* terms, const int4* items,
+                                     int* sync, int32_t* err, hipStream_t s) {
+  const int big = 0x7FFFFFFF;
+  GemmArgs a13{xq, xs, row_src, S, off, E, w13, 2 * I, H, nullptr, 1, big,
+               g_gate, g_up, xgs, row_src, h, I};
+  a13.items = items;
+  GemmArgs a2{hq, hs, nullptr, R, off, E, w2, H, I, terms, 1, big};
+  a2.c_w = row_w;
+  a2.c_g = g_down;
+  a2.c_gs = hgs;
+  a2.items = items;
+  const int n13 = gemm_grid(2 * kGemmWaves, a13, R);
+  const int n2 = gemm_grid(2 * kGemmWaves, a2, R);
+  const int groups = n13 / items_per_group<true, 2, kGemmWaves>(a13);
+  const LayerSync f{n13, groups, sync, sync + n13, err, hq, hs, hgs};
+  const size_t l13 = gemm_lds_bytes(H, kPassRows), l2 = gemm_lds_bytes(I, kPassRows);
+  const size_t lds = l13 > l2 ? l13 : l2;
+  auto kern = I <= 1024 ? k_gemm_layer<MOE_GEMM_D, 8, 1> : k_gemm_layer<MOE_GEMM_D, 8, 2>;
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(n13 + kQuantParts * groups + n2), dim3(64 * kGemmWaves), lds, s,
+                     a13, a2, f);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------- W4A16

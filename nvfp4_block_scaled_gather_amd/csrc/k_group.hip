@@ -361,7 +361,8 @@ __global__ __launch_bounds__(kGroupThreads) void k_group(
 
 // Grouping (block 0) and NVFP4 quantization of the S source rows of x (the other blocks,
 // 1024 / nthreads rows each) in one launch: the two are independent, since a row's codes
-// depend only on the row.
+// depend only on the row.  Block 0 also clears zero[0 .. nzero) (the next launch's
+// counters).
 template <int BPT>
 __global__ __launch_bounds__(kGroupThreads) void k_group_quantize(
     const int32_t* __restrict__ a_expert, const int32_t* __restrict__ a_src,
@@ -370,10 +371,12 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_quantize(
     float* __restrict__ row_w, int32_t* __restrict__ tok_off, int32_t* __restrict__ tok_rows,
     int32_t* __restrict__ err_word, bool parallel, bool cached,
     const uint16_t* __restrict__ x, int H, int nthreads, uint8_t* __restrict__ xq,
-    uint8_t* __restrict__ xs, float* __restrict__ xgs, int4* __restrict__ items) {
+    uint8_t* __restrict__ xs, float* __restrict__ xgs, int4* __restrict__ items,
+    int* __restrict__ zero, int nzero) {
   extern __shared__ __attribute__((aligned(16))) int lds[];
   __shared__ float s_red[kGroupWaves];
   if (blockIdx.x == 0) {
+    for (int k = threadIdx.x; k < nzero; k += kGroupThreads) zero[k] = 0;
     if (R <= kSmallGroupRows)  // (no work list: the GEMMs scan the offsets)
       group_small(a_expert, a_src, a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst,
                   row_w, tok_off, tok_rows, err_word);
@@ -447,7 +450,8 @@ hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, 
                                  int32_t* expert_offsets, int32_t* row_src, int32_t* row_dst,
                                  float* row_w, int32_t* tok_off, int32_t* tok_rows,
                                  int32_t* err_word, const uint16_t* x, int H, uint8_t* xq,
-                                 uint8_t* xs, float* xgs, int4* items, hipStream_t s) {
+                                 uint8_t* xs, float* xgs, int4* items, hipStream_t s, int* zero,
+                                 int nzero) {
   const bool par = group_parallel(E, T), cached = group_cached(E, T, R);
   const int NB = H / 16, nt = row_threads(NB);
   const int rows_per_block = kGroupThreads / nt;
@@ -458,13 +462,15 @@ hipError_t launch_group_quantize(const int32_t* a_expert, const int32_t* a_src, 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_group_quantize<1>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
                        a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
-                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs, items);
+                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs, items, zero,
+                       nzero);
   } else {
     const hipError_t e = set_lds(k_group_quantize<2>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_group_quantize<2>, grid, dim3(kGroupThreads), lds, s, a_expert, a_src,
                        a_dst, a_w, R, E, S, T, expert_offsets, row_src, row_dst, row_w, tok_off,
-                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs, items);
+                       tok_rows, err_word, par, cached, x, H, nt, xq, xs, xgs, items, zero,
+                       nzero);
   }
   return hipGetLastError();
 }

@@ -925,11 +925,12 @@ void k_gemm_mfma(GemmArgs p) {
 // nothing measurable.  The arithmetic of every output is k_gemm_mfma's and k_quantize's, so
 // the results are the bits of the separate launches.
 struct LayerSync {
-  int n13;         // workgroups of the w13 GEMM: n13 / groups per group
-  int groups;      // group slots (min(E, R)): kQuantParts quantization workgroups each,
-                   // then the w2 GEMM's workgroups
+  int n13;         // workgroups of the w13 GEMM: `groups` slots of n13 / groups items each
+  int groups;      // group slots (min(E, R)); kQuantParts quantization workgroups each
+                   // follow the w13 range, then the w2 GEMM's workgroups
   int* done13;     // [n13] nonzero once w13 item slot b has written its part of h
-  int* ready;      // [kQuantParts x groups] nonzero once part j of group a is quantized
+  int* ready;      // [kQuantParts x groups]: entry kQuantParts a + j nonzero once part j
+                   // of group a is quantized
   int32_t* err;    // device error word
   uint8_t* hq;     // NVFP4 h: codes [R, I/2], scales [R, I/16], row globals [R]
   uint8_t* hs;

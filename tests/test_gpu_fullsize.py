@@ -150,45 +150,58 @@ def test_full_size_layer_equals_separate_calls(lib, full_weights, name):
 # group sizes of the one-launch GEMM pair's test batch: multi-pass groups (double passes,
 # a single pass after them, four quantization parts), one exactly 16 rows, small groups
 ONE_LAUNCH_SIZES = [61, 41, 33, 17, 16, 12, 9, 5, 3, 2, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1]
+ONE_LAUNCH_EXPERTS = [3, 150, 77, 11, 42, 99, 5, 120, 60, 159, 0, 1, 2, 40, 41, 100, 101, 130,
+                      131, 149]
 
 
-def _one_launch_batch(base, experts):
-    """The first sum(ONE_LAUNCH_SIZES) assignments of `base`, moved onto `experts` with
-    ONE_LAUNCH_SIZES rows each, in a shuffled order."""
+def _one_launch_batch(base, case):
+    """Assignments of `base` (its first R) moved onto chosen experts, in a shuffled order:
+    "groups": ONE_LAUNCH_SIZES rows on ONE_LAUNCH_EXPERTS; "edge": 65 groups of one row
+    (the smallest batch whose grid is large at these sizes); "invalid": "groups" with two
+    expert ids and one output row out of range (dropped, error bits set)."""
     from nvfp4_block_scaled_gather_amd import workloads as W
-    R = sum(ONE_LAUNCH_SIZES)
-    a_expert = np.repeat(np.asarray(experts, np.int32), ONE_LAUNCH_SIZES)
+    if case == "edge":
+        a_expert = np.arange(0, 2 * 65, 2, dtype=np.int32)
+    else:
+        a_expert = np.repeat(np.asarray(ONE_LAUNCH_EXPERTS, np.int32), ONE_LAUNCH_SIZES)
+    R = len(a_expert)
     np.random.default_rng(7).shuffle(a_expert)
+    a_dst = base.a_dst[:R].copy()
+    if case == "invalid":
+        a_expert[[4, 90]] = [base.E, -1]
+        a_dst[17] = base.T
     return W.Workload(**{**base.__dict__, "a_expert": a_expert, "a_src": base.a_src[:R],
-                         "a_dst": base.a_dst[:R], "a_w": base.a_w[:R]})
+                         "a_dst": a_dst, "a_w": base.a_w[:R]})
 
 
-@pytest.mark.parametrize("I", [1024, 2048])
-def test_one_launch_gemm_pair_equals_separate_calls(lib, full_weights, I):
+@pytest.mark.parametrize("I,case", [(1024, "groups"), (2048, "groups"), (2048, "edge"),
+                                    (2048, "invalid")])
+def test_one_launch_gemm_pair_equals_separate_calls(lib, full_weights, I, case):
     """A batch that fills both GEMMs' large grid (min(E, R) times I / 64 and H / 128 items
     above 2048) runs the w13 GEMM, the quantization of h and the w2 GEMM in one launch: the
     w13 items flag their parts of h, four quantization workgroups per group wait for the
     group's flags, and the w2 items wait for their group's quantization ([MF], the fusion of
     the two grouped GEMMs).  Bit-identical to the separate entry points, twice in a row (the
-    flags are cleared for each call), over 20 of E experts with groups of 1 to 61 rows, with
-    one (I = 1024) and two (I = 2048) scale blocks per lane in the quantization of h, and no
-    error bit (a wait that gave up would set MOE_ERR_SYNC)."""
+    flags are cleared for each call): groups of 1 to 61 rows on 20 of E experts, with one
+    (I = 1024) and two (I = 2048) scale blocks per lane in the quantization of h; 65 groups
+    of one row (the smallest such batch); dropped assignments (their error bits, and never
+    MOE_ERR_SYNC, which a wait that gave up would set)."""
     from nvfp4_block_scaled_gather_amd import binding as B
     from nvfp4_block_scaled_gather_amd import layer as L
     from nvfp4_block_scaled_gather_amd import workloads as W
     E = 288 if I == 2048 else 160
     base = W.make_workload("ragged570", E=E, H=4096, I=I)
-    experts = [3, 150, 77, 11, 42, 99, 5, 120, 60, 159, 0, 1, 2, 40, 41, 100, 101, 130, 131, 149]
-    wl = _one_launch_batch(base, experts)
-    say("one-launch GEMM pair vs separate calls", "E=%d I=%d R=%d" % (E, I, wl.R))
+    wl = _one_launch_batch(base, case)
+    say("one-launch GEMM pair vs separate calls", case, "E=%d I=%d R=%d" % (E, I, wl.R))
     assert min(wl.E, wl.R) * min(I // 64, 4096 // 128) > 2048
     weights = full_weights if I == 2048 else None
     dl = L.DeviceLayer(wl, flags=0, gemv_max_rows=0, weights=weights,
                        experts=None if weights else wl.active_experts())
     want = composed_layer(B, dl, 0, 0)
+    err_want = B.MOE_ERR_EXPERT | B.MOE_ERR_DST if case == "invalid" else 0
     for rep in range(2):
         got = host(dl.forward()).copy()
-        assert dl.device_error() == 0
+        assert dl.device_error() == err_want
         assert np.array_equal(got, want), rep
 
 

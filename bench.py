@@ -227,7 +227,8 @@ READ_PROBE_VARIANTS = {0: "contiguous per wave, 8 KiB in flight, 32 waves/CU",
                        1: "contiguous per wave, 16 KiB in flight, 32 waves/CU",
                        2: "contiguous per wave, 16 KiB in flight, 16 waves/CU",
                        3: "the w13 GEMM's items: 4 waves x 2 tiles of 36 KiB, 4 KiB of each "
-                          "in flight"}
+                          "in flight",
+                       4: "contiguous per wave, 32 KiB in flight, 32 waves/CU"}
 
 
 def read_roofline(iters, settle_ms=0.0):

@@ -321,7 +321,8 @@ int moe_layer_forward_w4a16(const moe_layer_desc* L, const uint16_t* x, int S,
  * variant (0 <= variant < moe_hbm_read_probe_variants()): 0, 1, 2: each wave streams a
  *   contiguous run with 8, 16 or 16 KiB of loads in flight, 32, 32 or 16 waves per CU;
  *   3: the w13 GEMM's pattern: one workgroup of 4 waves per 288 KiB item of 8 tiles of
- *   36 KiB, each wave walking two tiles side by side with 4 KiB of each in flight.
+ *   36 KiB, each wave walking two tiles side by side with 4 KiB of each in flight;
+ *   4: contiguous runs with 32 KiB in flight per wave, 32 waves per CU.
  * bytes: a positive multiple of 294,912 (one such item); src 16-byte aligned.
  * sink: one device uint32, written only if a lane's XOR of the data it read equals `key`
  *   (it keeps the loads alive; its value means nothing).

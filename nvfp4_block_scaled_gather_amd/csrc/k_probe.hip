@@ -5,7 +5,7 @@
 //
 // Two load patterns, both non-temporal 16-byte loads per lane (each byte read once):
 //  * k_read_stream<U>: every wave owns a contiguous run of 1 KiB pieces (a wave-wide load
-//    covers 1 KiB) and keeps U pieces in flight;
+//    covers 1 KiB) and keeps U pieces in flight (U = 8, 16, 32);
 //  * k_read_items<D>: the grouped GEMM's pattern: a workgroup of 4 waves covers 8
 //    consecutive 36 KiB tiles (one work item of the w13 GEMM at K = 4096), each wave
 //    walking two tiles side by side, 1 KiB at a time, with D pieces of each in flight.
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_read_items(const uint8_t* __r
   fold_store(acc, key, sink);
 }
 
-int probe_variants() { return 4; }
+int probe_variants() { return 5; }
 
 hipError_t launch_read_probe(const uint8_t* src, size_t bytes, int variant, uint32_t key,
                              uint32_t* sink, hipStream_t s) {
@@ -108,9 +108,15 @@ hipError_t launch_read_probe(const uint8_t* src, size_t bytes, int variant, uint
       hipLaunchKernelGGL(k_read_stream<16>, dim3(1024), dim3(kProbeThreads), 0, s, src,
                          (long long)(bytes / 16384), key, sink);
       break;
-    default:  // the GEMM's items, 4 pieces of each tile in flight per wave
+    case 3:  // the GEMM's items, 4 pieces of each tile in flight per wave
       hipLaunchKernelGGL(k_read_items<4>, dim3((unsigned)(bytes / kItemBytes)),
                          dim3(kProbeThreads), 0, s, src, key, sink);
+      break;
+    default:  // 8 workgroups (32 waves) per CU, 32 KiB in flight per wave: measured on
+              // MI355X the fastest of these patterns (1% above 16 KiB; cached instead of
+              // non-temporal loads were 12% slower, 64 KiB with 16 waves per CU 9%)
+      hipLaunchKernelGGL(k_read_stream<32>, dim3(2048), dim3(kProbeThreads), 0, s, src,
+                         (long long)(bytes / 32768), key, sink);
       break;
   }
   return hipGetLastError();

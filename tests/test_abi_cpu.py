@@ -144,7 +144,7 @@ def test_argument_errors_are_reported_before_launch(lib):
 def test_read_probe_rejects_bad_arguments_before_launch(lib):
     p16 = ctypes.c_void_p(4096)
     n = lib.moe_hbm_read_probe_variants()
-    assert n == 4
+    assert n == 5
     unit = 294912
     assert lib.moe_hbm_read_probe(p16, unit + 16, 0, 0, p16, None) == B.MOE_EUNSUPPORTED
     assert lib.moe_hbm_read_probe(p16, 0, 0, 0, p16, None) == B.MOE_EUNSUPPORTED

@@ -565,7 +565,7 @@ def test_scatter_within_bf16_rounding(lib):
 
 
 # ------------------------------------------------------------------------------ read probe
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 def test_read_probe_reads_every_byte_it_is_given(lib, variant):
     """moe_hbm_read_probe (the measured read roofline) reads the whole buffer: one 16-byte
     word planted at the first, a middle and the last position is seen (the sink takes the

@@ -62,9 +62,9 @@ enum {
 };
 
 /* bits of the device error word.  MOE_ERR_SYNC: inside moe_layer_forward's one-launch
- * GEMM pair (batches that fill the large grid), a w2 workgroup gave up waiting for its
- * group's quantized rows of h (a bounded wait that does not end in a correct run); that
- * call's output is then not valid. */
+ * GEMM pair (batches of more than 32 assignments), a workgroup gave up waiting for the
+ * work it depends on (its group's part of h, or the group's quantized rows of h: a bounded
+ * wait that does not end in a correct run); that call's output is then not valid. */
 enum { MOE_ERR_EXPERT = 1, MOE_ERR_SRC = 2, MOE_ERR_DST = 4, MOE_ERR_SYNC = 8 };
 
 /* ----------------------------------------------------------------------------------
@@ -232,8 +232,9 @@ int moe_scatter_add(const float* y, int R, int H, const int32_t* expert_offsets,
  * The w2 GEMM writes each row's weighted scatter term, summed per token by the last launch;
  * with at most 16 assignments (and I <= 1024 or I = 2048; also I = 3072 or 4096 with at
  * most 8 assignments) the w2 launch sums each token's terms itself, and the layer is two
- * launches.  A batch that fills the large grid on the MFMA path (more than 64 assignments
- * and more than 64 experts, H and I multiples of 1024, I <= 2048) runs the w13 GEMM, the
+ * launches.  A batch of more than 32 assignments on the MFMA path (H and I multiples of
+ * 1024, I <= 2048, and H = 2I or else min(E, R)·I/64 and min(E, R)·H/128 on the same side
+ * of 2048; otherwise the five launches of the steps) runs the w13 GEMM, the
  * quantization of h and the w2 GEMM as one launch ([MF], the fusion of the two grouped
  * GEMMs): the w2 workgroups start as the w13 GEMM's last workgroups finish, each waiting,
  * with a bounded wait, until its group's rows of h are quantized (MOE_ERR_SYNC if a wait

@@ -391,7 +391,7 @@ int run_layer(const moe_layer_desc* L, const uint16_t* x, int S, const int32_t* 
                                  one_launch ? w.nsync : 0);
   if (e != hipSuccess) return hip_status(e, "layer: group+quantize launch");
   if (one_launch) {
-    // a batch that fills the large grid: w13 + SwiGLU, the quantization of h and w2 in one
+    // more than 32 assignments: w13 + SwiGLU, the quantization of h and w2 in one
     // launch (h in its own buffer, since the w2 items write their terms into acc while
     // other groups' rows of h are still read), then the per-token sum; the same bits
     e = moe::launch_grouped_gemm_layer(w.xq, w.xs, w.row_src, S, w.offsets, E, R,

@@ -31,7 +31,7 @@
 // SwiGLU epilogue, each workgroup grouping the assignments and quantizing its group's
 // source rows itself) and k_gemm_quantizing (w2, each workgroup quantizing its rows of h).
 // k_gemm_layer runs the layer's two GEMMs and the quantization of h between them as one
-// launch for batches that fill the large grid (k_gemm_mfma's items, flags between them).
+// launch for batches of more than 32 assignments (k_gemm_mfma's items, flags between them).
 //
 // Outputs are written as whole rows of the workgroup's block (store_out): measured on
 // MI355X, write-back stores that are later evicted from L2 in the middle of the weight
@@ -902,7 +902,7 @@ void k_gemm_mfma(GemmArgs p) {
 
 // ------------------------------------------------------------------------- fused layer
 // The layer's w13 GEMM (SwiGLU epilogue), the NVFP4 quantization of h and the w2 GEMM
-// (scatter-ready epilogue) in one launch, for batches that fill the large grid.  The grid
+// (scatter-ready epilogue) in one launch, for batches of more than 32 assignments.  The grid
 // is three ranges, each in the work list's order: [0, n13) the w13 items, then one
 // quantization workgroup per group, then the w2 items.  A w13 item raises its own flag once
 // its part of h is written; a group's quantization workgroup waits for the flags of the
@@ -1021,8 +1021,12 @@ __device__ __forceinline__ void quantize_h_rows(const uint16_t* h, int I, int r0
   }
 }
 
-template <int D, int S, int BPT>
-__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(4)))
+// D13, NS2, D2: the w13 GEMM's ring depth and the w2 GEMM's tiles per wave and ring depth,
+// those of the separate launches' instances for the same grid (large: 4, 2, 4; small:
+// 8, 1, 8).
+template <int D13, int NS2, int D2, int S, int BPT>
+__global__ __launch_bounds__(64 * kGemmWaves)
+__attribute__((amdgpu_waves_per_eu(D13 > 4 ? 1 : 4)))
 void k_gemm_layer(GemmArgs p13, GemmArgs p2, LayerSync f) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int s_grp[4];
@@ -1031,7 +1035,7 @@ void k_gemm_layer(GemmArgs p13, GemmArgs p2, LayerSync f) {
   const int ipe13 = items_per_group<true, 2, kGemmWaves>(p13);
   if (b < f.n13) {  // uniform: a w13 item
     if (!find_group<kPassRows>(p13, b / ipe13, s_grp, g)) return;  // uniform
-    run_item<2, D, S, true, false, kGemmWaves, kPassRows>(p13, b % ipe13, g, smem);
+    run_item<2, D13, S, true, false, kGemmWaves, kPassRows>(p13, b % ipe13, g, smem);
     raise_flag(f.done13 + b);
     return;
   }
@@ -1047,13 +1051,14 @@ void k_gemm_layer(GemmArgs p13, GemmArgs p2, LayerSync f) {
     return;
   }
   // a w2 item
-  const int ipe2 = items_per_group<false, 2, kGemmWaves>(p2);
+  const int ipe2 = items_per_group<false, NS2, kGemmWaves>(p2);
   const int item = b - f.n13 - kQuantParts * f.groups;
   const int* ready = f.ready + kQuantParts * (item / ipe2);
   const int v = load_flags(ready, kQuantParts);
   if (!find_group<kPassRows>(p2, item / ipe2, s_grp, g)) return;  // uniform
   wait_flags(v, ready, kQuantParts, f.err);
-  run_item<2, D, S, false, false, kGemmWaves, kPassRows, kDeviceScope>(p2, item % ipe2, g, smem);
+  run_item<NS2, D2, S, false, false, kGemmWaves, kPassRows, kDeviceScope>(p2, item % ipe2, g,
+                                                                          smem);
 }
 
 // ------------------------------------------------------------------------- decode w13
@@ -1870,7 +1875,8 @@ bool grouped_gemm_layer_fits(int E, int R, int H, int I) {
   a2.E = E;
   a2.N = H;
   a2.K = I;
-  return !small_grid(a13, R) && !small_grid(a2, R);
+  // (the two GEMMs on the same kind of grid, so that one instance serves both)
+  return small_grid(a13, R) == small_grid(a2, R);
 }
 
 int grouped_gemm_layer_sync_ints(int E, int R, int H, int I) {
@@ -1900,13 +1906,19 @@ hipError_t launch_grouped_gemm_layer(const uint8_t* xq, const uint8_t* xs, const
   a2.c_g = g_down;
   a2.c_gs = hgs;
   a2.items = items;
+  // the separate launches' instances: a small grid (decode batches of 33 to 64 rows at
+  // 288 experts) takes the deeper ring and, in w2, one tile per wave
+  const bool small = small_grid(a13, R);
   const int n13 = gemm_grid(2 * kGemmWaves, a13, R);
-  const int n2 = gemm_grid(2 * kGemmWaves, a2, R);
+  const int n2 = gemm_grid((small ? 1 : 2) * kGemmWaves, a2, R);
   const int groups = n13 / items_per_group<true, 2, kGemmWaves>(a13);
   const LayerSync f{n13, groups, sync, sync + n13, err, hq, hs, hgs};
-  const size_t l13 = gemm_lds_bytes(H, kPassRows), l2 = gemm_lds_bytes(I, kPassRows);
+  const size_t l13 = gemm_lds_bytes(H, kPassRows),
+               l2 = gemm_lds_bytes(I, kPassRows, false, small ? 1 : 2);
   const size_t lds = l13 > l2 ? l13 : l2;
-  auto kern = I <= 1024 ? k_gemm_layer<MOE_GEMM_D, 8, 1> : k_gemm_layer<MOE_GEMM_D, 8, 2>;
+  auto kern = small ? (I <= 1024 ? k_gemm_layer<8, 1, 8, 8, 1> : k_gemm_layer<8, 1, 8, 8, 2>)
+                    : (I <= 1024 ? k_gemm_layer<MOE_GEMM_D, 2, MOE_GEMM_D, 8, 1>
+                                 : k_gemm_layer<MOE_GEMM_D, 2, MOE_GEMM_D, 8, 2>);
   if (lds > 65536) {
     const hipError_t e = hipFuncSetAttribute((const void*)kern,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

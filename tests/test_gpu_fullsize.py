@@ -157,11 +157,15 @@ ONE_LAUNCH_EXPERTS = [3, 150, 77, 11, 42, 99, 5, 120, 60, 159, 0, 1, 2, 40, 41, 
 def _one_launch_batch(base, case):
     """Assignments of `base` (its first R) moved onto chosen experts, in a shuffled order:
     "groups": ONE_LAUNCH_SIZES rows on ONE_LAUNCH_EXPERTS; "edge": 65 groups of one row
-    (the smallest batch whose grid is large at these sizes); "invalid": "groups" with two
+    (the smallest batch whose grid is large at these sizes); "small": 40 rows in 9 groups
+    (a small grid: the decode instances); "invalid": "groups" with two
     expert ids and one output row out of range (dropped, error bits set)."""
     from nvfp4_block_scaled_gather_amd import workloads as W
     if case == "edge":
         a_expert = np.arange(0, 2 * 65, 2, dtype=np.int32)
+    elif case == "small":
+        a_expert = np.repeat(np.asarray(ONE_LAUNCH_EXPERTS[:9], np.int32),
+                             [17, 9, 5, 3, 2, 1, 1, 1, 1])
     else:
         a_expert = np.repeat(np.asarray(ONE_LAUNCH_EXPERTS, np.int32), ONE_LAUNCH_SIZES)
     R = len(a_expert)
@@ -175,17 +179,18 @@ def _one_launch_batch(base, case):
 
 
 @pytest.mark.parametrize("I,case", [(1024, "groups"), (2048, "groups"), (2048, "edge"),
-                                    (2048, "invalid")])
+                                    (2048, "small"), (2048, "invalid")])
 def test_one_launch_gemm_pair_equals_separate_calls(lib, full_weights, I, case):
-    """A batch that fills both GEMMs' large grid (min(E, R) times I / 64 and H / 128 items
-    above 2048) runs the w13 GEMM, the quantization of h and the w2 GEMM in one launch: the
+    """A batch of more than 32 assignments (H and I multiples of 1024, I <= 2048) runs the
+    w13 GEMM, the quantization of h and the w2 GEMM in one launch: the
     w13 items flag their parts of h, four quantization workgroups per group wait for the
     group's flags, and the w2 items wait for their group's quantization ([MF], the fusion of
     the two grouped GEMMs).  Bit-identical to the separate entry points, twice in a row (the
     flags are cleared for each call): groups of 1 to 61 rows on 20 of E experts, with one
     (I = 1024) and two (I = 2048) scale blocks per lane in the quantization of h; 65 groups
-    of one row (the smallest such batch); dropped assignments (their error bits, and never
-    MOE_ERR_SYNC, which a wait that gave up would set)."""
+    of one row (the smallest batch on the large grid); 40 rows (a small grid); dropped
+    assignments (their error bits, and never MOE_ERR_SYNC, which a wait that gave up would
+    set)."""
     from nvfp4_block_scaled_gather_amd import binding as B
     from nvfp4_block_scaled_gather_amd import layer as L
     from nvfp4_block_scaled_gather_amd import workloads as W
@@ -193,7 +198,7 @@ def test_one_launch_gemm_pair_equals_separate_calls(lib, full_weights, I, case):
     base = W.make_workload("ragged570", E=E, H=4096, I=I)
     wl = _one_launch_batch(base, case)
     say("one-launch GEMM pair vs separate calls", case, "E=%d I=%d R=%d" % (E, I, wl.R))
-    assert min(wl.E, wl.R) * min(I // 64, 4096 // 128) > 2048
+    assert wl.R > 32
     weights = full_weights if I == 2048 else None
     dl = L.DeviceLayer(wl, flags=0, gemv_max_rows=0, weights=weights,
                        experts=None if weights else wl.active_experts())

@@ -365,18 +365,19 @@ def test_full_size_w4a16_sampled_tokens(lib, full_weights, name):
 
 def test_graph_replay_matches_eager(lib):
     """A captured layer replays to the eager output bit for bit, replay after replay, with
-    eager work between replays (no memset nodes are recorded: the one-launch GEMM pair's
-    counters, in the last case, are cleared by the grouping kernel)."""
+    eager work between replays (no memset nodes are recorded: the flags of the one-launch
+    GEMM pair, in the last two cases on its large and its small grid, are cleared by the
+    grouping kernel)."""
     import torch
     from nvfp4_block_scaled_gather_amd import layer as L
     from nvfp4_block_scaled_gather_amd import workloads as W
     for name, dims in (("tiny", {}), ("ragged570", dict(E=32, H=512, I=256)),
                        ("zipf512", dict(E=48, H=256, I=256)),
                        ("decode2", dict(E=32, H=512, I=1024)),
-                       ("ragged570", dict(E=160, H=4096, I=1024))):
+                       ("ragged570", dict(E=160, H=4096, I=1024)), ("decode8", {})):
         say("graph", name, dims)
         wl = W.make_workload(name, **dims)
-        dl = L.DeviceLayer(wl)
+        dl = L.DeviceLayer(wl, experts=wl.active_experts())
         want = dl.forward().clone()
         sync()
         graph = dl.capture_graph()
